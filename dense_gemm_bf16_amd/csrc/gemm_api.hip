@@ -1,0 +1,310 @@
+// C-ABI front end of the bf16 GEMM library: argument checks, the choice of
+// kernel configuration, split-K workspaces, launch.  The contract of every
+// entry point is stated in include/gemm_bf16.h.
+#include "../../include/gemm_bf16.h"
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "gemm_internal.h"
+
+namespace gemm {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return GEMM_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- workspaces
+// One split-K workspace per (device, stream): [counters | partials].  The
+// counters are zeroed once at allocation; every call leaves them at zero.
+struct Workspace {
+  int device;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+
+std::mutex g_ws_mu;
+std::vector<Workspace> g_ws;
+
+constexpr size_t kCounterBytes = 64 * 1024;  // 16384 tile counters
+constexpr size_t kMaxCounters = kCounterBytes / sizeof(uint32_t);
+
+int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (Workspace& w : g_ws) {
+    if (w.device != device || w.stream != stream) continue;
+    if (w.bytes >= bytes) {
+      *out = w.ptr;
+      return GEMM_OK;
+    }
+    // grow: the old buffer may still be in use by work queued on `stream`
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipFree(w.ptr);
+    if (e != hipSuccess) return hip_fail(e);
+    w.ptr = nullptr;
+    w.bytes = 0;
+    e = hipMalloc(&w.ptr, bytes);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMemset(w.ptr, 0, kCounterBytes);
+    if (e != hipSuccess) return hip_fail(e);
+    w.bytes = bytes;
+    *out = w.ptr;
+    return GEMM_OK;
+  }
+  Workspace w{device, stream, nullptr, 0};
+  hipError_t e = hipMalloc(&w.ptr, bytes);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipMemset(w.ptr, 0, kCounterBytes);
+  if (e != hipSuccess) {
+    hipFree(w.ptr);
+    return hip_fail(e);
+  }
+  w.bytes = bytes;
+  g_ws.push_back(w);
+  *out = w.ptr;
+  return GEMM_OK;
+}
+
+size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
+  if (p.splits <= 1) return 0;
+  const int64_t tiles = ((M + p.tile->bm - 1) / p.tile->bm) * ((N + p.tile->bn - 1) / p.tile->bn);
+  return kCounterBytes + (size_t)tiles * p.splits * p.tile->bm * p.tile->bn * sizeof(float);
+}
+
+// ------------------------------------------------------------ config choice
+// Static shape -> configuration rules.  The large square and prefill shapes
+// have enough 256x256 tiles to fill the 256 CUs; the M = 256 decode shapes
+// do not, so K is split across workgroups until the grid covers the chip.
+constexpr int kCUs = 256;
+
+int choose_splits(int64_t tiles, int64_t k_tiles) {
+  if (tiles >= kCUs || k_tiles < 8) return 1;
+  int s = (int)((kCUs + tiles - 1) / tiles);
+  // keep at least 4 K-steps of 64 per slice
+  while (s > 1 && k_tiles / s < 4) --s;
+  return s < 1 ? 1 : s;
+}
+
+void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + p->tile->bm - 1) / p->tile->bm) * ((N + p->tile->bn - 1) / p->tile->bn);
+  const int64_t k_tiles = (K + kBK - 1) / kBK;
+  if (p->splits > k_tiles) p->splits = (int)(k_tiles > 0 ? k_tiles : 1);
+  if (p->splits < 1) p->splits = 1;
+  if (p->splits > 1) {
+    // equal slices of ceil(k_tiles / S) steps; drop slices left empty
+    const int64_t per = (k_tiles + p->splits - 1) / p->splits;
+    p->splits = (int)((k_tiles + per - 1) / per);
+  }
+  if ((size_t)tiles > kMaxCounters) p->splits = 1;
+  snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
+}
+
+Plan choose_plan(int64_t M, int64_t N, int64_t K) {
+  Plan p{};
+  const TileConfig* big = find_tile_config("t256x256_w2x2_s2_x1");
+  const TileConfig* small = find_tile_config("t128x128_w2x2_s3_x1");
+  p.tile = (M <= 128 && N <= 1024) ? small : big;
+  const int64_t tiles = ((M + p.tile->bm - 1) / p.tile->bm) * ((N + p.tile->bn - 1) / p.tile->bn);
+  p.splits = choose_splits(tiles, (K + kBK - 1) / kBK);
+  p.group_m = 4;
+  finish_plan(&p, M, N, K);
+  return p;
+}
+
+// Parse "tile[_k<splits>][_g<group>]" where tile is a table name.
+bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out) {
+  char buf[64];
+  if (strlen(name) >= sizeof buf) return false;
+  strcpy(buf, name);
+  int splits = 1, group = 4;
+  for (;;) {
+    char* u = strrchr(buf, '_');
+    if (!u) break;
+    int v = 0;
+    if (u[1] == 'k' && sscanf(u + 2, "%d", &v) == 1 && v >= 1) {
+      splits = v;
+      *u = 0;
+    } else if (u[1] == 'g' && sscanf(u + 2, "%d", &v) == 1 && v >= 1) {
+      group = v;
+      *u = 0;
+    } else {
+      break;
+    }
+  }
+  const TileConfig* t = find_tile_config(buf);
+  if (!t) return false;
+  out->tile = t;
+  out->splits = splits;
+  out->group_m = group;
+  finish_plan(out, M, N, K);
+  return true;
+}
+
+// ----------------------------------------------------------------- checks
+int check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const void* C, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || ldc < N) return GEMM_ERR_INVALID_ARG;
+  if (M > 0 && N > 0) {
+    if (!C) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && (!A || !B)) return GEMM_ERR_INVALID_ARG;
+  }
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15) return GEMM_ERR_MISALIGNED;
+  if ((lda | ldb | ldc) & 7) return GEMM_ERR_MISALIGNED;
+  return GEMM_OK;
+}
+
+int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+        const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, hipStream_t stream) {
+  if (M == 0 || N == 0) return GEMM_OK;
+  const TileConfig& t = *p.tile;
+  // 32-bit limits: tile-relative byte offsets of the operands, grid size,
+  // and the int32 shape fields of the kernel.
+  if ((int64_t)t.bm * lda * 2 >= (int64_t(1) << 31) || (int64_t)t.bn * ldb * 2 >= (int64_t(1) << 31))
+    return GEMM_ERR_UNSUPPORTED;
+  if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31))
+    return GEMM_ERR_UNSUPPORTED;
+  const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
+  const int64_t k_tiles = (K + kBK - 1) / kBK;
+  const int64_t grid = tiles_m * tiles_n * p.splits;
+  if (grid >= (int64_t(1) << 31)) return GEMM_ERR_UNSUPPORTED;
+
+  KernelArgs a{};
+  a.A = (const uint16_t*)A;
+  a.B = (const uint16_t*)B;
+  a.C = C;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.tiles_m = (int32_t)tiles_m;
+  a.tiles_n = (int32_t)tiles_n;
+  a.k_tiles = (int32_t)k_tiles;
+  a.splits = p.splits;
+  a.k_tiles_per_split = (int32_t)((k_tiles + p.splits - 1) / p.splits);
+  a.group_m = p.group_m;
+  int flags = out_f32 ? kOutF32 : 0;
+  if ((K & 7) != 0) flags |= kRaggedK;
+  if (p.splits > 1) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    void* ws = nullptr;
+    int rc = get_workspace(dev, stream, workspace_bytes(p, M, N), &ws);
+    if (rc != GEMM_OK) return rc;
+    a.counters = (uint32_t*)ws;
+    a.partials = (float*)((char*)ws + kCounterBytes);
+    flags |= kSplitK;
+  }
+  hipError_t e = t.launch(a, (int)grid, stream, flags);
+  if (e != hipSuccess) return hip_fail(e);
+  return GEMM_OK;
+}
+
+int gemm_entry(const char* config, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+               const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, void* stream) {
+  int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != GEMM_OK) return rc;
+  Plan p{};
+  if (config && config[0]) {
+    if (!plan_from_name(config, M, N, K, &p)) return GEMM_ERR_UNSUPPORTED;
+  } else {
+    p = choose_plan(M, N, K);
+  }
+  return run(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32, (hipStream_t)stream);
+}
+
+thread_local char g_name_buf[64];
+
+}  // namespace
+}  // namespace gemm
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+              int64_t ldb, void* C, int64_t ldc, void* stream) {
+  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, false, stream);
+}
+
+int gemm_bf16_f32out(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, true, stream);
+}
+
+int gemm_bf16_ex(const char* config, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                 const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* stream) {
+  return gemm::gemm_entry(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32 != 0, stream);
+}
+
+const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return "invalid";
+  gemm::Plan p = gemm::choose_plan(M, N, K);
+  memcpy(gemm::g_name_buf, p.name, sizeof p.name);
+  return gemm::g_name_buf;
+}
+
+const char* gemm_bf16_config_at(int i) {
+  if (i < 0) return nullptr;
+  const gemm::TileConfig* t = gemm::tile_configs();
+  for (int j = 0; j < i; ++j)
+    if (!t[j].name) return nullptr;
+  return t[i].name;
+}
+
+const char* gemm_bf16_status_string(int status) {
+  switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_ERR_INVALID_ARG: return "invalid argument (negative size, ld too small, or NULL)";
+    case GEMM_ERR_MISALIGNED: return "misaligned (pointers need 16 B, leading dims a multiple of 8)";
+    case GEMM_ERR_UNSUPPORTED: return "unsupported (size beyond 32-bit offsets, or unknown config)";
+    case GEMM_ERR_HIP: return "HIP runtime error (see gemm_bf16_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int gemm_bf16_last_hip_error(void) { return gemm::g_last_hip_error; }
+
+int gemm_bf16_reserve_workspace(size_t bytes, void* stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return gemm::hip_fail(e);
+  void* ws = nullptr;
+  const size_t need = bytes < gemm::kCounterBytes ? gemm::kCounterBytes : bytes;
+  return gemm::get_workspace(dev, (hipStream_t)stream, need, &ws);
+}
+
+size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K < 0) return 0;
+  gemm::Plan p = gemm::choose_plan(M, N, K);
+  return gemm::workspace_bytes(p, M, N);
+}
+
+int gemm_bf16_release_workspace(void) {
+  std::lock_guard<std::mutex> lk(gemm::g_ws_mu);
+  int rc = GEMM_OK;
+  for (gemm::Workspace& w : gemm::g_ws) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) cur = w.device;
+    hipSetDevice(w.device);
+    hipError_t e = hipStreamSynchronize(w.stream);
+    if (e == hipSuccess) e = hipFree(w.ptr);
+    if (e != hipSuccess) rc = gemm::hip_fail(e);
+    hipSetDevice(cur);
+  }
+  gemm::g_ws.clear();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Host-side description of the kernel configurations the library is built
+// with, shared between the launcher table and the C-ABI front end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gemm_kernel.hpp"
+
+namespace gemm {
+
+// One compiled tile configuration.  `launch` takes the variant flags
+// (kOutF32 | kSplitK | kRaggedK) and enqueues the matching kernel.
+struct TileConfig {
+  const char* name;  // e.g. "t256x256_w2x2_s2_x1"
+  int bm, bn;        // output tile
+  int threads;       // workgroup size
+  int lds_bytes;     // static LDS per workgroup
+  hipError_t (*launch)(const KernelArgs&, int grid, hipStream_t, int flags);
+};
+
+// Table of built configurations, terminated by an entry with name == NULL.
+const TileConfig* tile_configs();
+
+const TileConfig* find_tile_config(const char* name);
+
+// A complete launch plan: tile config, split count and raster grouping.
+struct Plan {
+  const TileConfig* tile;
+  int splits;
+  int group_m;
+  char name[64];
+};
+
+}  // namespace gemm

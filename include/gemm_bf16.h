@@ -1,0 +1,131 @@
+/*
+ * gemm_bf16 -- dense bf16 GEMM for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ *   C[M,N] = A[M,K] * B[N,K]^T      bf16 inputs, fp32 accumulation,
+ *                                   bf16 output (or fp32 for the debug call)
+ *
+ * The operation is the one defined on the page "Matrix Multiplication on
+ * NVIDIA's Blackwell: A Four-Part Deep Dive" (section on the definition of
+ * matrix multiplication: C is M x N inner products over K; naive-kernel
+ * section: the second operand is read as b[col, k], bf16 in and out with the
+ * sum carried in fp32), and the linear-layer matmul of transformer prefill
+ * and decode from the page "Hand-writing a Blackwell GEMM: from 164 to 1400
+ * TFLOP/s" (section "two workloads, not one").  There is no alpha/beta: C is
+ * overwritten with the product, as in that page's K-loop step, where a C tile
+ * is the sum of A_k B_k^T starting from zero.
+ *
+ * Layouts.  All strides are in elements; all pointers are device pointers
+ * on the current HIP device (hipGetDevice at the time of the call).
+ *   A(m,k) = A[m*lda + k], lda >= K   (row-major, K contiguous)
+ *   B(n,k) = B[n*ldb + k], ldb >= K   ("K-major": N rows of K)
+ *   C(m,n) = C[m*ldc + n], ldc >= N   (row-major)
+ * bf16 values are raw 16-bit patterns (uint16_t or __hip_bfloat16 storage).
+ *
+ * Shapes.  Any M, N, K >= 0.  M == 0 or N == 0: nothing is launched, the
+ * call returns GEMM_OK.  K == 0: C is set to zeros (the empty sum).
+ *
+ * Alignment (required): A, B and C 16-byte aligned; lda, ldb and ldc
+ * multiples of 8 elements.  Otherwise GEMM_ERR_MISALIGNED.
+ *
+ * Numerics.  Products of bf16 values are exact in fp32; sums are fp32 in an
+ * order fixed by the chosen configuration (so results are bitwise
+ * reproducible run to run, split-K included).  The bf16 output is the fp32
+ * sum rounded to nearest, ties to even.
+ *
+ * Ownership.  The caller owns A, B and C; the library neither frees nor
+ * retains them.  C must not overlap A or B.  The library owns a split-K
+ * workspace per (device, stream): allocated on first need, grown when a
+ * larger one is needed (growth synchronises that stream), freed by
+ * gemm_bf16_release_workspace.  Pre-size it with gemm_bf16_reserve_workspace
+ * before stream capture, since allocation cannot be captured.
+ *
+ * Streams and errors.  Calls are asynchronous: work is enqueued on `stream`
+ * (a hipStream_t passed as void*, NULL = the null stream) and the call never
+ * synchronises it, except when growing a workspace.  Argument errors are
+ * returned synchronously before anything is enqueued.  A device fault shows
+ * up at the caller's next synchronisation.  Calls on different streams may
+ * run concurrently.  Nothing aborts and nothing prints.
+ */
+#ifndef GEMM_BF16_H
+#define GEMM_BF16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point that returns int. */
+#define GEMM_OK 0
+#define GEMM_ERR_INVALID_ARG 1 /* negative size, ld too small, NULL with work */
+#define GEMM_ERR_MISALIGNED 2  /* pointer not 16 B aligned or ld % 8 != 0 */
+#define GEMM_ERR_UNSUPPORTED 3 /* operand too large for 32-bit tile offsets,
+                                  unknown config name */
+#define GEMM_ERR_HIP 4         /* a HIP runtime call failed; see
+                                  gemm_bf16_last_hip_error */
+
+/* C = A * B^T with bf16 output.  Arguments as described above.  Returns a
+ * status code. */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void* A, int64_t lda,
+              const void* B, int64_t ldb,
+              void* C, int64_t ldc,
+              void* stream);
+
+/* Debug variant: the same product with the fp32 sums stored unrounded.
+ * C is float*, 16 B aligned, ldc in floats (a multiple of 8).  Same
+ * configuration choice and summation order as
+ * gemm_bf16 for the same shape, so rounding this output to bf16 gives
+ * gemm_bf16's result. */
+int gemm_bf16_f32out(int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda,
+                     const void* B, int64_t ldb,
+                     float* C, int64_t ldc,
+                     void* stream);
+
+/* As gemm_bf16 / gemm_bf16_f32out, but with the kernel configuration named
+ * explicitly (one of the names gemm_bf16_config_at enumerates), for
+ * ablations, tuning sweeps and tests that compare configurations.
+ * config == NULL or "" selects automatically.  out_f32 != 0 writes fp32 to C
+ * (then C is float*).  Unknown name: GEMM_ERR_UNSUPPORTED. */
+int gemm_bf16_ex(const char* config,
+                 int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 void* C, int64_t ldc,
+                 int out_f32, void* stream);
+
+/* Name of the configuration gemm_bf16 would choose for this shape (tile
+ * sizes, pipeline depth, split count), e.g. "t256x256_s2_k1".  Static
+ * storage; never NULL. */
+const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K);
+
+/* Enumerate the built configurations: the i-th name, or NULL past the end. */
+const char* gemm_bf16_config_at(int i);
+
+/* Human-readable text for a status code.  Static storage; never NULL. */
+const char* gemm_bf16_status_string(int status);
+
+/* The hipError_t value of the most recent failed HIP call made by this
+ * library on the calling thread (0 if none). */
+int gemm_bf16_last_hip_error(void);
+
+/* Make sure the workspace of (current device, stream) holds at least
+ * `bytes` bytes, allocating now rather than inside a later gemm call.
+ * Returns a status code. */
+int gemm_bf16_reserve_workspace(size_t bytes, void* stream);
+
+/* Bytes of workspace the automatic choice needs for this shape (0 when it
+ * does not split K). */
+size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Free every workspace this library holds, on every device.  Synchronises
+ * the streams they belong to first.  Returns a status code. */
+int gemm_bf16_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_BF16_H */

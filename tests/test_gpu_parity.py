@@ -1,0 +1,220 @@
+"""GPU parity: the HIP library against the oracle, element by element.
+
+Gates (bf16 in, fp32 sums, bf16 out):
+* integer-valued inputs: bit-exact bf16 and exact fp32 debug output;
+* N(0,1)-type inputs: within 1 bf16 ulp of the oracle's rounded result, or
+  within 1e-4 * sqrt(K) * sigma_A * sigma_B of the exact sum near zero;
+* fp32 debug output: within 1e-4 * sqrt(K) * sigma_A * sigma_B.
+
+Shapes are those of the workloads in ``synthetic_inputs``: 512^3, 4096^3,
+the M = 8192 prefill and M = 256 decode linear layers, the 512 x 8192 x 5376
+projection and ragged M in {1, 17, 64, 200}; plus edge cases.  Every call
+goes through the C ABI (``gemm_bf16_ex``) with the automatic configuration
+unless a test names one.
+"""
+import numpy as np
+import pytest
+
+from oracle.compare import check_bf16, check_f32
+from synthetic_inputs import WORKLOADS, int_bf16, normal_bf16
+from tests.gpu_util import run_gemm
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle():
+    import oracle
+
+    return oracle
+
+
+def _full_check(w, A, B, exact):
+    o = _oracle()
+    ref16, ref64 = o.gemm(A, B, K=w.K)
+    got = run_gemm(A, B, K=w.K)
+    rep = check_bf16(got, ref16, ref64, w.K, w.sigma_a, w.sigma_b, exact=exact)
+    print(w.name, "bf16", rep, flush=True)
+    assert rep["ok"], rep
+    got32 = run_gemm(A, B, K=w.K, out_f32=True)
+    rep32 = check_f32(got32, ref64, w.K, w.sigma_a, w.sigma_b, exact=exact)
+    print(w.name, "f32", rep32, flush=True)
+    assert rep32["ok"], rep32
+
+
+@pytest.mark.parametrize("name", ["square512_int", "square512_normal"])
+def test_square512(name):
+    w = WORKLOADS[name]
+    A, B = w.make()
+    _full_check(w, A, B, exact=(w.dist == "int"))
+
+
+@pytest.mark.parametrize("name", ["square4096_int", "square4096_normal"])
+def test_square4096_full(name):
+    w = WORKLOADS[name]
+    A, B = w.make()
+    _full_check(w, A, B, exact=(w.dist == "int"))
+
+
+@pytest.mark.parametrize("name", ["decode_attn_out", "decode_qkv", "decode_mlp_up",
+                                  "decode_mlp_down"])
+def test_decode_full(name):
+    w = WORKLOADS[name]
+    A, B = w.make()
+    o = _oracle()
+    ref16, ref64 = o.gemm(A, B, K=w.K)
+    got = run_gemm(A, B)
+    rep = check_bf16(got, ref16, ref64, w.K, w.sigma_a, w.sigma_b)
+    print(name, rep, flush=True)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("name", ["proj_512x8192x5376", "ragged_m1", "ragged_m17",
+                                  "ragged_m64", "ragged_m200"])
+def test_irregular_full(name):
+    w = WORKLOADS[name]
+    A, B = w.make()
+    o = _oracle()
+    ref16, ref64 = o.gemm(A, B, K=w.K)
+    got = run_gemm(A, B)
+    rep = check_bf16(got, ref16, ref64, w.K, w.sigma_a, w.sigma_b)
+    print(name, rep, flush=True)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("name", ["prefill_attn_out", "prefill_mlp_up"])
+def test_prefill_sampled(name):
+    """Full rows and full columns of the product (the oracle cannot afford
+    all of it in test time): the first and last 32 rows/columns (edge tiles)
+    plus 32 spread through the middle."""
+    w = WORKLOADS[name]
+    A, B = w.make()
+    got = run_gemm(A, B)
+    o = _oracle()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(w.M - 32, w.M),
+                                     rng.choice(w.M, 32, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(32), np.arange(w.N - 32, w.N),
+                                     rng.choice(w.N, 32, replace=False)]))
+    r16, r64 = o.gemm(np.ascontiguousarray(A[rows]), B, K=w.K)
+    rep = check_bf16(got[rows], r16, r64, w.K, w.sigma_a, w.sigma_b)
+    print(name, "rows", rep, flush=True)
+    assert rep["ok"], rep
+    c16, c64 = o.gemm(A, np.ascontiguousarray(B[cols]), K=w.K)
+    rep = check_bf16(got[:, cols], c16, c64, w.K, w.sigma_a, w.sigma_b)
+    print(name, "cols", rep, flush=True)
+    assert rep["ok"], rep
+
+
+# ------------------------------------------------------------- edge cases
+
+def test_every_config_bit_exact_on_ragged_shape():
+    """Each built tile configuration, with and without split-K, on a shape
+    that is ragged in M, N and K: integer inputs, so bit-exact."""
+    import dense_gemm_bf16_amd as g
+
+    M, N, K = 300, 520, 456
+    A = int_bf16(M, K, seed=101)
+    B = int_bf16(N, K, seed=102)
+    ref16, ref64 = _oracle().gemm(A, B)
+    for cfg in g.config_names():
+        for split in (1, 3):
+            name = f"{cfg}_k{split}"
+            got = run_gemm(A, B, config=name)
+            rep = check_bf16(got, ref16, None, K, exact=True)
+            print(name, rep, flush=True)
+            assert rep["ok"], (name, rep)
+
+
+@pytest.mark.parametrize("K", [1, 7, 8, 17, 63, 65, 200])
+def test_ragged_k(K):
+    """K not a multiple of 8 (a 16-byte chunk straddles K) and not of 64;
+    the padding of A and B holds NaN, which must never be read."""
+    M, N = 70, 90
+    lda = ldb = ((K + 7) // 8) * 8 + 8
+    A = np.full((M, lda), 0x7FC0, np.uint16)
+    B = np.full((N, ldb), 0x7FC0, np.uint16)
+    A[:, :K] = int_bf16(M, K, seed=200 + K)
+    B[:, :K] = int_bf16(N, K, seed=300 + K)
+    ref16, ref64 = _oracle().gemm(A, B, K=K)
+    got = run_gemm(A, B, K=K)
+    rep = check_bf16(got, ref16, None, K, exact=True)
+    assert rep["ok"], rep
+    got32 = run_gemm(A, B, K=K, out_f32=True)
+    assert check_f32(got32, ref64, K, exact=True)["ok"]
+
+
+@pytest.mark.parametrize("N", [8, 24, 8200, 1000])
+def test_ragged_n_and_small_m(N):
+    A = normal_bf16(17, 264, seed=400)
+    B = normal_bf16(N, 264, seed=401)
+    ref16, ref64 = _oracle().gemm(A, B)
+    got = run_gemm(A, B)
+    rep = check_bf16(got, ref16, ref64, 264)
+    assert rep["ok"], rep
+
+
+def test_no_writes_outside_c():
+    """C sits inside a canary-filled buffer with ldc > N and a spare row on
+    each side; only the M x N window may change."""
+    M, N, K = 130, 200, 96
+    A = int_bf16(M, K, seed=500)
+    B = int_bf16(N, K, seed=501)
+    ref16, _ = _oracle().gemm(A, B)
+    canary = 0x5A5A
+    buf = run_gemm(A, B, ldc=216, canary=canary)
+    assert buf.shape == (M + 2, 216)
+    assert np.all(buf[0] == canary) and np.all(buf[-1] == canary)
+    assert np.all(buf[1:-1, N:] == canary)
+    assert np.array_equal(buf[1:-1, :N], ref16)
+
+
+def test_k_zero_gives_zeros():
+    import torch
+
+    import dense_gemm_bf16_amd as g
+
+    C = torch.full((5, 16), 1234, dtype=torch.int16, device="cuda")
+    g.gemm_bf16(5, 16, 0, None, 8, None, 8, C, 16)
+    torch.cuda.synchronize()
+    assert not C.cpu().numpy().any()
+
+
+def test_empty_m_or_n_is_noop():
+    import dense_gemm_bf16_amd as g
+
+    g.gemm_bf16(0, 16, 8, None, 8, None, 8, None, 16)
+    g.gemm_bf16(4, 0, 8, None, 8, None, 8, None, 8)
+
+
+def test_split_k_matches_unsplit_on_integers():
+    """Decode shape with integer inputs: split and unsplit both bit-exact."""
+    M, N, K = 256, 1024, 8192
+    A = int_bf16(M, K, seed=600)
+    B = int_bf16(N, K, seed=601)
+    ref16, _ = _oracle().gemm(A, B)
+    for cfg in ["t256x256_w2x2_s2_x1_k1", "t256x256_w2x2_s2_x1_k8",
+                "t256x256_w2x2_s2_x1_k5"]:
+        got = run_gemm(A, B, config=cfg)
+        assert check_bf16(got, ref16, None, K, exact=True)["ok"], cfg
+
+
+def test_deterministic_repeat():
+    """Two calls give identical bits (fixed summation order, split-K too)."""
+    w = WORKLOADS["decode_attn_out"]
+    A, B = w.make()
+    a = run_gemm(A, B)
+    b = run_gemm(A, B)
+    assert np.array_equal(a, b)
+
+
+def test_identity_and_k1_closed_forms():
+    """A = I gives B^T exactly; K = 1 gives RNE(a*b) exactly, any bf16."""
+    K = 64
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80
+    B = normal_bf16(40, K, seed=700)
+    assert np.array_equal(run_gemm(eye, B), B.T)
+    a = normal_bf16(50, 1, seed=701)
+    b = normal_bf16(30, 1, seed=702)
+    ref16, _ = _oracle().gemm(a, b)
+    assert np.array_equal(run_gemm(a, b, K=1), ref16)
