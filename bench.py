@@ -77,26 +77,27 @@ def measured_traffic(workload: str, config: str):
 
 
 def cpu_baseline(w, A, B, target_s: float):
-    """The oracle (as it stands) on the first R rows of this workload."""
+    """The oracle (as it stands) on the first R rows of this workload: the
+    whole workload if it fits the time target, else as many rows as do."""
     import oracle
 
     threads = oracle.max_threads()
-    rows = min(w.M, 4)
+    rows = min(w.M, 64)
     t0 = time.perf_counter()
     oracle.gemm(A[:rows], B, K=w.K, want_f64=False)
-    dt = time.perf_counter() - t0
-    per_row = dt / rows
+    per_row = (time.perf_counter() - t0) / rows
     R = int(max(1, min(w.M, target_s / max(per_row, 1e-9))))
     t0 = time.perf_counter()
     oracle.gemm(A[:R], B, K=w.K, want_f64=False)
     dt = time.perf_counter() - t0
+    what = "all" if R == w.M else f"first {R} of {w.M}"
     return {
         "value": round(gemm_flops(R, w.N, w.K) / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {R} of {w.M} rows of A: {R}x{w.N}x{w.K} GEMM, fp64 sums "
-                  f"({dt:.1f} s on {threads} threads, {os.cpu_count()} logical CPUs)",
+        "sample": f"{what} rows of A: {R}x{w.N}x{w.K} GEMM, fp64 sums, "
+                  f"{dt:.1f} s on {threads} OpenMP threads ({os.cpu_count()} logical CPUs)",
     }
 
 
@@ -107,7 +108,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square4096_normal")
     ap.add_argument("--config", default=None, help="force a kernel configuration")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target length of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--context", action="store_true",

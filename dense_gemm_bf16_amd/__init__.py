@@ -119,14 +119,17 @@ def config_name(M, N, K) -> str:
     return _lib.gemm_bf16_config_name(M, N, K).decode()
 
 
+def config_at(i: int):
+    """The i-th built configuration name, or None past the end."""
+    n = _lib.gemm_bf16_config_at(i)
+    return None if n is None else n.decode()
+
+
 def config_names() -> list[str]:
-    out, i = [], 0
-    while True:
-        n = _lib.gemm_bf16_config_at(i)
-        if n is None:
-            return out
-        out.append(n.decode())
-        i += 1
+    out = []
+    while (n := config_at(len(out))) is not None:
+        out.append(n)
+    return out
 
 
 def status_string(status: int) -> str:
@@ -147,6 +150,16 @@ def workspace_size(M, N, K) -> int:
 
 def release_workspace() -> None:
     _check(_lib.gemm_bf16_release_workspace())
+
+
+# The C names, for callers who prefer them.
+gemm_bf16_config_name = config_name
+gemm_bf16_config_at = config_at
+gemm_bf16_status_string = status_string
+gemm_bf16_last_hip_error = last_hip_error
+gemm_bf16_reserve_workspace = reserve_workspace
+gemm_bf16_workspace_size = workspace_size
+gemm_bf16_release_workspace = release_workspace
 
 
 def matmul(A, B, out=None, out_f32=False, config=None, stream=None):

@@ -23,8 +23,9 @@ int hip_fail(hipError_t e) {
 }
 
 // ---------------------------------------------------------------- workspaces
-// One split-K workspace per (device, stream): [counters | partials].  The
-// counters are zeroed once at allocation; every call leaves them at zero.
+// One split-K workspace per (device, stream), holding the fp32 partial
+// products of the K-slices.  Work on one stream runs in order, so one buffer
+// per stream is never used by two calls at once.
 struct Workspace {
   int device;
   hipStream_t stream;
@@ -34,9 +35,6 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
-
-constexpr size_t kCounterBytes = 64 * 1024;  // 16384 tile counters
-constexpr size_t kMaxCounters = kCounterBytes / sizeof(uint32_t);
 
 int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
@@ -55,8 +53,6 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
     w.bytes = 0;
     e = hipMalloc(&w.ptr, bytes);
     if (e != hipSuccess) return hip_fail(e);
-    e = hipMemset(w.ptr, 0, kCounterBytes);
-    if (e != hipSuccess) return hip_fail(e);
     w.bytes = bytes;
     *out = w.ptr;
     return GEMM_OK;
@@ -64,40 +60,50 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
   Workspace w{device, stream, nullptr, 0};
   hipError_t e = hipMalloc(&w.ptr, bytes);
   if (e != hipSuccess) return hip_fail(e);
-  e = hipMemset(w.ptr, 0, kCounterBytes);
-  if (e != hipSuccess) {
-    hipFree(w.ptr);
-    return hip_fail(e);
-  }
   w.bytes = bytes;
   g_ws.push_back(w);
   *out = w.ptr;
   return GEMM_OK;
 }
 
+int64_t partial_ld(int64_t N) { return (N + 7) / 8 * 8; }
+
 size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
   if (p.splits <= 1) return 0;
-  const int64_t tiles = ((M + p.tile->bm - 1) / p.tile->bm) * ((N + p.tile->bn - 1) / p.tile->bn);
-  return kCounterBytes + (size_t)tiles * p.splits * p.tile->bm * p.tile->bn * sizeof(float);
+  return (size_t)p.splits * (size_t)M * (size_t)partial_ld(N) * sizeof(float);
 }
 
 // ------------------------------------------------------------ config choice
-// Static shape -> configuration rules.  The large square and prefill shapes
-// have enough 256x256 tiles to fill the 256 CUs; the M = 256 decode shapes
-// do not, so K is split across workgroups until the grid covers the chip.
+// Static shape -> configuration rules, from measurements on MI355X (the
+// sweeps are summarised in the design notes):
+//  * enough 256x256 tiles to fill the 256 CUs (4096^3, M = 8192 prefill):
+//    the eight-wave ping-pong kernel, no split;
+//  * very small M (decode batches up to 64 rows): the same kernel with K
+//    split so that about 256 workgroups stream B;
+//  * otherwise (M of a few hundred, e.g. the M = 256 decode layers and the
+//    512-row projection): 128x128 tiles, K split until about 256 workgroups.
 constexpr int kCUs = 256;
+constexpr const char* kBigTile = "t256x256x32_w2x4_s4_x2_p2";
+constexpr const char* kMidTile = "t128x128x64_w2x2_s4_x2_p1";
 
+int64_t tiles_of(const TileConfig* t, int64_t M, int64_t N) {
+  return ((M + t->bm - 1) / t->bm) * ((N + t->bn - 1) / t->bn);
+}
+
+// Splits so that tiles * splits is about the CU count, keeping at least 8
+// K-steps per slice.
 int choose_splits(int64_t tiles, int64_t k_tiles) {
-  if (tiles >= kCUs || k_tiles < 8) return 1;
-  int s = (int)((kCUs + tiles - 1) / tiles);
-  // keep at least 4 K-steps of 64 per slice
-  while (s > 1 && k_tiles / s < 4) --s;
+  if (tiles >= kCUs) return 1;
+  int s = (int)((kCUs + tiles / 2) / tiles);
+  while (s > 1 && k_tiles / s < 8) --s;
   return s < 1 ? 1 : s;
 }
 
 void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + p->tile->bm - 1) / p->tile->bm) * ((N + p->tile->bn - 1) / p->tile->bn);
-  const int64_t k_tiles = (K + kBK - 1) / kBK;
+  (void)M;
+  (void)N;
+  const int64_t bk = p->tile->bk;
+  const int64_t k_tiles = (K + bk - 1) / bk;
   if (p->splits > k_tiles) p->splits = (int)(k_tiles > 0 ? k_tiles : 1);
   if (p->splits < 1) p->splits = 1;
   if (p->splits > 1) {
@@ -105,17 +111,21 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
     const int64_t per = (k_tiles + p->splits - 1) / p->splits;
     p->splits = (int)((k_tiles + per - 1) / per);
   }
-  if ((size_t)tiles > kMaxCounters) p->splits = 1;
   snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
 }
 
 Plan choose_plan(int64_t M, int64_t N, int64_t K) {
   Plan p{};
-  const TileConfig* big = find_tile_config("t256x256_w2x2_s2_x1");
-  const TileConfig* small = find_tile_config("t128x128_w2x2_s3_x1");
-  p.tile = (M <= 128 && N <= 1024) ? small : big;
-  const int64_t tiles = ((M + p.tile->bm - 1) / p.tile->bm) * ((N + p.tile->bn - 1) / p.tile->bn);
-  p.splits = choose_splits(tiles, (K + kBK - 1) / kBK);
+  const TileConfig* big = find_tile_config(kBigTile);
+  const TileConfig* mid = find_tile_config(kMidTile);
+  const int64_t big_tiles = tiles_of(big, M, N);
+  if (big_tiles >= kCUs - kCUs / 8 || M <= 64) {
+    p.tile = big;
+    p.splits = choose_splits(big_tiles, (K + big->bk - 1) / big->bk);
+  } else {
+    p.tile = mid;
+    p.splits = choose_splits(tiles_of(mid, M, N), (K + mid->bk - 1) / mid->bk);
+  }
   p.group_m = 4;
   finish_plan(&p, M, N, K);
   return p;
@@ -175,7 +185,7 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31))
     return GEMM_ERR_UNSUPPORTED;
   const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
-  const int64_t k_tiles = (K + kBK - 1) / kBK;
+  const int64_t k_tiles = (K + t.bk - 1) / t.bk;
   const int64_t grid = tiles_m * tiles_n * p.splits;
   if (grid >= (int64_t(1) << 31)) return GEMM_ERR_UNSUPPORTED;
 
@@ -197,19 +207,25 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   a.group_m = p.group_m;
   int flags = out_f32 ? kOutF32 : 0;
   if ((K & 7) != 0) flags |= kRaggedK;
+  void* ws = nullptr;
   if (p.splits > 1) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
-    void* ws = nullptr;
     int rc = get_workspace(dev, stream, workspace_bytes(p, M, N), &ws);
     if (rc != GEMM_OK) return rc;
-    a.counters = (uint32_t*)ws;
-    a.partials = (float*)((char*)ws + kCounterBytes);
+    a.C = ws;
+    a.ldc = partial_ld(N);
+    a.c_split_stride = M * a.ldc;
     flags |= kSplitK;
   }
   hipError_t e = t.launch(a, (int)grid, stream, flags);
   if (e != hipSuccess) return hip_fail(e);
+  if (p.splits > 1) {
+    e = launch_splitk_reduce((const float*)ws, a.ldc, a.c_split_stride, p.splits, C, ldc,
+                             (int)M, (int)N, out_f32, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return GEMM_OK;
 }
 
@@ -281,8 +297,7 @@ int gemm_bf16_reserve_workspace(size_t bytes, void* stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return gemm::hip_fail(e);
   void* ws = nullptr;
-  const size_t need = bytes < gemm::kCounterBytes ? gemm::kCounterBytes : bytes;
-  return gemm::get_workspace(dev, (hipStream_t)stream, need, &ws);
+  return gemm::get_workspace(dev, (hipStream_t)stream, bytes < 256 ? 256 : bytes, &ws);
 }
 
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {

@@ -13,8 +13,9 @@ namespace gemm {
 // One compiled tile configuration.  `launch` takes the variant flags
 // (kOutF32 | kSplitK | kRaggedK) and enqueues the matching kernel.
 struct TileConfig {
-  const char* name;  // e.g. "t256x256_w2x2_s2_x1"
+  const char* name;  // e.g. "t256x256x64_w2x2_s2_x2"
   int bm, bn;        // output tile
+  int bk;            // K elements per ring slot
   int threads;       // workgroup size
   int lds_bytes;     // static LDS per workgroup
   hipError_t (*launch)(const KernelArgs&, int grid, hipStream_t, int flags);
@@ -32,5 +33,11 @@ struct Plan {
   int group_m;
   char name[64];
 };
+
+// Fixed-order fp32 sum of S partial buffers P + s*slice_stride (rows of
+// stride ldp) into C, rounded to bf16 or stored as fp32.
+hipError_t launch_splitk_reduce(const float* P, int64_t ldp, int64_t slice_stride, int S,
+                                void* C, int64_t ldc, int M, int N, bool out_f32,
+                                hipStream_t stream);
 
 }  // namespace gemm

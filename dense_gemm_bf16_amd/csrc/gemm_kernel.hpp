@@ -12,45 +12,52 @@
 //     "Matrix Multiplication on NVIDIA's Blackwell", Kernel 9: thread-block
 //     swizzle for L2 reuse; the XCD split is specific to this chip.)
 //
-//  2. Global -> LDS staging through an S-slot ring.  Each K-step of BK = 64
-//     copies A[m0:m0+BM, k:k+64] and B[n0:n0+BN, k:k+64] (rows of 128 bytes)
-//     into one ring slot with buffer_load ... lds (16 bytes per lane, straight
-//     into LDS, no VGPR round trip).  Loads for step t+S-1 are in flight while
-//     step t computes.  (Page "Hand-writing a Blackwell GEMM", Step 2: a
-//     multi-stage shared-memory pipeline; page "Matrix Multiplication on
-//     NVIDIA's Blackwell", Kernel 6: a ring of stages.)  Out-of-range rows
-//     and K-chunks read as zero through the buffer resource's range check.
+//  2. Global -> LDS staging through an S-slot ring.  Each K-step of BK
+//     elements copies A[m0:m0+BM, k:k+BK] and B[n0:n0+BN, k:k+BK] (rows of
+//     2*BK bytes) into one ring slot with buffer_load ... lds (16 bytes per
+//     lane, straight into LDS, no VGPR round trip).  A slot is refilled as
+//     soon as every wave has read its last fragments, so up to S-1 K-steps of
+//     loads are in flight ahead of the MFMAs.  (Page "Hand-writing a
+//     Blackwell GEMM", Step 2: a multi-stage shared-memory pipeline; page
+//     "Matrix Multiplication on NVIDIA's Blackwell", Kernel 6: a ring of
+//     stages.)  Out-of-range rows and K-chunks read as zero through the
+//     buffer resource's range check.
 //
-//  3. XOR swizzle.  Within each 128-byte LDS row the 16-byte chunk index is
-//     XORed with a function of the row, a permutation inside the row, so the
-//     reads of one 16-byte column across consecutive rows land in different
-//     LDS banks.  (Page "Hand-writing a Blackwell GEMM", Step 4: 128B
-//     swizzle; page "Matrix Multiplication on NVIDIA's Blackwell", appendix
-//     on the swizzle functor: bits 7-9 of the byte offset XORed into bits
-//     4-6.)  The LDS-DMA writes each lane's 16 bytes at a fixed position, so
-//     the swizzle is applied by choosing which global chunk each lane fetches.
+//  3. XOR swizzle.  Within each LDS row the 16-byte chunk index is XORed
+//     with a function of the row, a permutation inside the row, so the
+//     ds_read_b128 fragment reads of one chunk column across 16 consecutive
+//     rows (one LDS access phase of 16 lanes over 64 banks) land in 16
+//     different 16-byte bank groups.  (Page "Hand-writing a Blackwell GEMM",
+//     Step 4: 128B swizzle; page "Matrix Multiplication on NVIDIA's
+//     Blackwell", appendix on the swizzle functor: high address bits XORed
+//     into the 16-byte chunk bits.)  The LDS-DMA writes each lane's 16 bytes
+//     at a fixed position, so the swizzle is applied by choosing which
+//     global chunk each lane fetches.
 //
 //  4. MFMA.  Each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held as
-//     32x32 fp32 blocks in registers, and per 16-wide K-step issues
-//     v_mfma_f32_32x32x16_bf16 on fragments read from LDS with ds_read_b128.
-//     The MFMA's first operand is taken from B and the second from A, so a
-//     lane's accumulator holds four consecutive columns of one row of C,
-//     which makes the output stores row-contiguous.  (Page "Hand-writing a
-//     Blackwell GEMM", Step 1: C_tile = sum_k A_k B_k^T.)
+//     32x32 fp32 blocks in accumulator registers, and per 16-wide K substep
+//     issues v_mfma_f32_32x32x16_bf16 on fragments read from LDS with
+//     ds_read_b128.  The fragments of substep j+1 are read while substep j's
+//     MFMAs run; across K-steps too, because the ring barrier sits before
+//     the last substep.  The MFMA's first operand is taken from B and the
+//     second from A, so a lane's accumulator holds four consecutive columns
+//     of one row of C, which makes the output stores row-contiguous.  (Page
+//     "Hand-writing a Blackwell GEMM", Step 1: C_tile = sum_k A_k B_k^T.)
 //
-//  5. Split-K (when K is sliced): each slice writes its fp32 partial tile to
-//     a workspace, increments a per-tile counter, and the workgroup that
-//     arrives last adds the partials in slice order 0..S-1 (a fixed order, so
-//     results are reproducible) and runs the epilogue.  It then resets the
-//     counter to zero for the next call.
+//  5. Split-K (when the tiles alone cannot fill the chip): slice s of K
+//     writes its fp32 partial tile, unrounded, to partial buffer s; a
+//     separate reduction kernel (gemm_reduce.hip) then adds the slices in
+//     the fixed order 0..S-1 and rounds once, so results are reproducible.
 //
 //  6. Epilogue: fp32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32) and
 //     predicated stores of 4 consecutive columns per lane (or fp32 for the
-//     debug output).
+//     debug output and the split-K partials).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace gemm {
 
@@ -62,37 +69,66 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr int kBK = 64;                 // K elements per ring slot (128 B rows)
 constexpr uint32_t kOOB = 0x80000000u;  // voffset that fails the range check
 
 struct KernelArgs {
   const uint16_t* A;
   const uint16_t* B;
-  void* C;
-  int64_t lda, ldb, ldc;  // elements
+  void* C;                 // output, or the fp32 partial buffers when K is split
+  int64_t lda, ldb, ldc;   // elements
+  int64_t c_split_stride;  // elements between the partial buffers of two slices
   int32_t M, N, K;
   int32_t tiles_m, tiles_n;
-  int32_t k_tiles;            // ceil(K / kBK)
+  int32_t k_tiles;            // ceil(K / BK)
   int32_t splits;             // slices of K per tile (>= 1)
   int32_t k_tiles_per_split;  // every slice non-empty (host guarantees)
   int32_t group_m;            // raster group height in tiles
-  float* partials;            // splits > 1: tiles * splits * BM * BN floats
-  uint32_t* counters;         // splits > 1: one per tile, zero between calls
 };
 
-// Ring synchronisation: s_waitcnt vmcnt(N) lgkmcnt(0) then s_barrier.
-// After it, this wave has at most N vector-memory ops outstanding (the later
-// ring steps' loads) and no LDS op outstanding; after the barrier every wave
-// of the workgroup has done the same.  Written as one asm statement with a
-// memory clobber so that the compiler neither moves LDS accesses across it
-// nor adds waits of its own for the LDS-DMA loads (which it cannot see).
+// Variant flags of the kernel template.
+enum : int {
+  kOutF32 = 1,   // store the fp32 sums (debug output) instead of bf16
+  kSplitK = 2,   // K is sliced across workgroups; write fp32 partials
+  kRaggedK = 4,  // K % 8 != 0: patch the 16-byte chunk that straddles K
+};
+
+// ---------------------------------------------------------------- primitives
+
+// Wait until at most N vector-memory ops of this wave are outstanding and
+// all its LDS ops are done, then barrier the workgroup.  One asm statement
+// with a memory clobber, so that the compiler neither moves LDS accesses
+// across it nor adds waits of its own for the LDS-DMA loads, which it does
+// not see (they are issued from asm too).
 template <int N>
 __device__ __forceinline__ void ring_wait_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// ring_wait_barrier<STEP * n + OFF> for a run-time n in [0, MAXN].
+template <int STEP, int MAXN, int OFF>
+__device__ __forceinline__ void ring_wait_barrier_n_off(int n) {
+  if constexpr (MAXN <= 0) {
+    ring_wait_barrier<OFF>();
+  } else {
+    if (n >= MAXN) ring_wait_barrier<STEP * MAXN + OFF>();
+    else ring_wait_barrier_n_off<STEP, MAXN - 1, OFF>(n);
+  }
+}
+
+template <int STEP, int MAXN>
+__device__ __forceinline__ void ring_wait_barrier_n(int n) {
+  ring_wait_barrier_n_off<STEP, MAXN, 0>(n);
+}
+
+// ring_wait_barrier<STEP * n + (g ? G : 0)> for run-time n in [0, MAXN]
+// and a run-time flag g.
+template <int STEP, int MAXN, int G>
+__device__ __forceinline__ void ring_wait_barrier_ng(int n, bool g) {
+  if (g) ring_wait_barrier_n_off<STEP, MAXN, G>(n);
+  else ring_wait_barrier_n<STEP, MAXN>(n);
 }
 
 // 128-bit buffer resource (base, range in bytes) held in SGPRs.  Range
@@ -129,39 +165,51 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   return x * q + (x < r ? x : r) + i;
 }
 
-// 16-byte chunk permutation inside a 128-byte LDS row.
-template <int SWZ>
+// 16-byte chunk permutation inside an LDS row of CPR chunks (CPR = BK / 8).
+//   SWZ 0: none.
+//   SWZ 1: XOR with row mod CPR.
+//   SWZ 2: conflict-free for 16-lane phases over 64 four-byte banks: the
+//          16 rows of a phase cover 16 distinct (row-in-256-bytes, chunk)
+//          pairs.  128-byte rows: (row ^ row/8) mod 8; 64-byte rows:
+//          (row / 4) mod 4.
+template <int SWZ, int CPR>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (SWZ == 0) return 0;                      // no swizzle
-  else if constexpr (SWZ == 1) return row & 7;           // XOR with row mod 8
-  else return (row ^ (row >> 3)) & 7;                    // also folds row/8
+  if constexpr (SWZ == 0) return 0;
+  else if constexpr (SWZ == 1) return row & (CPR - 1);
+  else if constexpr (CPR == 8) return (row ^ (row >> 3)) & 7;
+  else return (row >> 2) & 3;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SWZ>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int SWZ>
 struct TileCfg {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int kWaveM = BM / WAVES_M;
   static constexpr int kWaveN = BN / WAVES_N;
   static constexpr int kFragM = kWaveM / 32;
   static constexpr int kFragN = kWaveN / 32;
-  static constexpr int kABytes = BM * kBK * 2;
-  static constexpr int kBBytes = BN * kBK * 2;
+  static constexpr int kRowBytes = BK * 2;
+  static constexpr int kCpr = BK / 8;   // 16-byte chunks per LDS row
+  static constexpr int kSub = BK / 16;  // 16-wide MFMA substeps per K-step
+  static constexpr int kABytes = BM * kRowBytes;
+  static constexpr int kBBytes = BN * kRowBytes;
   static constexpr int kStageBytes = kABytes + kBBytes;
   static constexpr int kLdsBytes = STAGES * kStageBytes;
   static constexpr int kLoadsA = kABytes / (kThreads * 16);
   static constexpr int kLoadsB = kBBytes / (kThreads * 16);
   static constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
-  static constexpr int kRowsPerLoad = kThreads / 8;  // rows one load round covers
+  static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
   static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile in 32-blocks");
   static_assert(kABytes % (kThreads * 16) == 0, "A tile splits into loads");
   static_assert(kBBytes % (kThreads * 16) == 0, "B tile splits into loads");
   static_assert(kLdsBytes <= 160 * 1024, "LDS is 160 KB per CU");
   static_assert(STAGES >= 2, "ring needs two slots");
-  static_assert(kLoadsPerStage * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(kLoadsPerStage * (STAGES - 1) < 64, "vmcnt range");
 };
 
-// Issue the LDS-DMA loads of one operand tile (rows x 64 k) into LDS at
-// byte address `dst`.  voff[i] holds row*ld*2 + chunk*16 (or kOOB for absent
+// ------------------------------------------------------------------- loads
+
+// Issue the LDS-DMA loads of one operand tile (rows x BK) into LDS at byte
+// address `dst`.  voff[i] holds row*ld*2 + chunk*16 (or kOOB for absent
 // rows); the K offset goes in soffset, so this is only for K-steps that lie
 // wholly inside K.
 template <int NLOADS, int THREADS>
@@ -212,72 +260,27 @@ __device__ __forceinline__ void fix_tail_chunks(lds_u8* dst, const int (&chunk)[
   }
 }
 
-// Variant flags of the kernel template.
-enum : int {
-  kOutF32 = 1,   // store the fp32 sums (debug output) instead of bf16
-  kSplitK = 2,   // K is sliced across workgroups; reduce through the workspace
-  kRaggedK = 4,  // K % 8 != 0: patch the 16-byte chunk that straddles K
-};
+// --------------------------------------------------------------- fragments
 
-template <typename Cfg, bool OUT_F32>
-__device__ __forceinline__ void store_tile(const KernelArgs& a,
-                                           const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                           int m_base, int n_base, int lane) {
-#pragma unroll
-  for (int fm = 0; fm < Cfg::kFragM; ++fm) {
-    const int m = m_base + fm * 32 + (lane & 31);
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int fn = 0; fn < Cfg::kFragN; ++fn) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // lane holds C[m][n .. n+3] in acc[fm][fn][4g .. 4g+3]
-        const int n = n_base + fn * 32 + 8 * g + 4 * (lane >> 5);
-        const f32x4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
-                         acc[fm][fn][4 * g + 3]};
-        if constexpr (OUT_F32) {
-          float* c = (float*)a.C + (int64_t)m * a.ldc + n;
-          if (n + 3 < a.N) {
-            *(f32x4*)c = v;
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (n + j < a.N) c[j] = v[j];
-          }
-        } else {
-          const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
-          const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
-          __bf16* c = (__bf16*)a.C + (int64_t)m * a.ldc + n;
-          if (n + 3 < a.N) {
-            *(bf16x4*)c = (bf16x4){lo[0], lo[1], hi[0], hi[1]};
-          } else {
-            const __bf16 e[4] = {lo[0], lo[1], hi[0], hi[1]};
-            for (int j = 0; j < 4; ++j)
-              if (n + j < a.N) c[j] = e[j];
-          }
-        }
-      }
-    }
-  }
-}
-
-// Read the MFMA fragments of one 16-wide K-substep from a ring slot.
+// Read the MFMA fragments of one 16-wide K substep from a ring slot.
 // Lane l supplies 8 consecutive k of row (l % 32) at 16-byte chunk
-// 2*kk + l/32 of that row's 128 bytes.
+// 2*kk + l/32 of that row.
 template <typename Cfg, int SWZ>
 __device__ __forceinline__ void read_frags(const lds_u8* sa, const lds_u8* sb, int kk, int wm,
                                            int wn, int lane, bf16x8 (&fa)[Cfg::kFragM],
                                            bf16x8 (&fb)[Cfg::kFragN]) {
   typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
+  constexpr int R = Cfg::kRowBytes, CPR = Cfg::kCpr;
   const int lrow = lane & 31, lhalf = lane >> 5;
 #pragma unroll
   for (int fm = 0; fm < Cfg::kFragM; ++fm) {
     const int row = wm * Cfg::kWaveM + fm * 32 + lrow;
-    fa[fm] = *(lds_frag*)(sa + row * 128 + (((2 * kk + lhalf) ^ swz<SWZ>(row)) << 4));
+    fa[fm] = *(lds_frag*)(sa + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
   }
 #pragma unroll
   for (int fn = 0; fn < Cfg::kFragN; ++fn) {
     const int row = wn * Cfg::kWaveN + fn * 32 + lrow;
-    fb[fn] = *(lds_frag*)(sb + row * 128 + (((2 * kk + lhalf) ^ swz<SWZ>(row)) << 4));
+    fb[fn] = *(lds_frag*)(sb + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
   }
 }
 
@@ -293,13 +296,117 @@ __device__ __forceinline__ void mfma_block(f32x16 (&acc)[Cfg::kFragM][Cfg::kFrag
       acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SWZ, int FLAGS>
+// Call f(lo, hi) with compile-time integral constants lo = w*L/F and
+// hi = (w+1)*L/F (empty range for w >= F), for a run-time w in [1, 4].
+template <int F, int L, typename Fn>
+__device__ __forceinline__ void constexpr_for_window(int w, Fn&& f) {
+  auto call = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    constexpr int lo = W < F ? W * L / F : L;
+    constexpr int hi = W < F ? (W + 1) * L / F : L;
+    f(std::integral_constant<int, lo>{}, std::integral_constant<int, hi>{});
+  };
+  switch (w) {
+    case 1: call(std::integral_constant<int, 1>{}); break;
+    case 2: call(std::integral_constant<int, 2>{}); break;
+    case 3: call(std::integral_constant<int, 3>{}); break;
+    default: call(std::integral_constant<int, 4>{}); break;
+  }
+}
+
+// The MFMAs of one substep with G loads spaced evenly between them: load q
+// goes after MFMA ceil((q+1)*n/G) - 1, and a scheduling barrier keeps each
+// load at its place in the MFMA stream.
+template <typename Cfg, int G, typename Dma>
+__device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                               const bf16x8 (&fa)[Cfg::kFragM],
+                                               const bf16x8 (&fb)[Cfg::kFragN], Dma&& dma) {
+  constexpr int n = Cfg::kFragM * Cfg::kFragN;
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    const int fm = j / Cfg::kFragN, fn = j % Cfg::kFragN;
+    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+#pragma unroll
+    for (int q = (j * G) / n; q < ((j + 1) * G) / n; ++q) {
+      dma(q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- epilogue
+
+template <typename Cfg, bool OUT_F32>
+__device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase,
+                                           const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                           int m_base, int n_base, int lane) {
+#pragma unroll
+  for (int fm = 0; fm < Cfg::kFragM; ++fm) {
+    const int m = m_base + fm * 32 + (lane & 31);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int fn = 0; fn < Cfg::kFragN; ++fn) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // lane holds C[m][n .. n+3] in acc[fm][fn][4g .. 4g+3]
+        const int n = n_base + fn * 32 + 8 * g + 4 * (lane >> 5);
+        const f32x4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
+                         acc[fm][fn][4 * g + 3]};
+        if constexpr (OUT_F32) {
+          float* c = (float*)Cbase + (int64_t)m * a.ldc + n;
+          if (n + 3 < a.N) {
+            *(f32x4*)c = v;
+          } else {
+            for (int j = 0; j < 4; ++j)
+              if (n + j < a.N) c[j] = v[j];
+          }
+        } else {
+          const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
+          __bf16* c = (__bf16*)Cbase + (int64_t)m * a.ldc + n;
+          if (n + 3 < a.N) {
+            *(bf16x4*)c = (bf16x4){lo[0], lo[1], hi[0], hi[1]};
+          } else {
+            const __bf16 e[4] = {lo[0], lo[1], hi[0], hi[1]};
+            for (int j = 0; j < 4; ++j)
+              if (n + j < a.N) c[j] = e[j];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernel
+
+// One workgroup per CU (the ring takes most of the 160 KB LDS): 4 waves run
+// one per SIMD, 8 waves two per SIMD.
+//
+// PIPE selects how the LDS-DMA loads of a K-step are issued:
+//   0 (burst):  all at once, right after the barrier that frees the slot;
+//   1, 3, 4 (spread): one by one between MFMAs, over the first F substeps
+//      of the window from that barrier to the next one (F = kSub, kSub-1,
+//      kSub-2 for PIPE 1, 3, 4).
+// A wave issues LDS-DMA loads at most about one per ~100 cycles (1 KB
+// each), and while it waits to issue one, its in-order instruction stream
+// cannot issue MFMAs either; a burst of loads therefore idles that SIMD's
+// MFMA pipe.  Spread issue with at least three MFMAs between loads keeps
+// the pipe busy.  With two ring slots, the loads of a step must land by the
+// barrier that ends its window, so they are packed into the first F
+// substeps and the rest of the window is latency slack.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int SWZ, int PIPE,
+          int FLAGS>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES_M * WAVES_N * 64,
                                                       WAVES_M * WAVES_N * 64),
-                          amdgpu_waves_per_eu(1, 1))) void
+                          amdgpu_waves_per_eu(WAVES_M * WAVES_N / 4,
+                                              WAVES_M * WAVES_N / 4))) void
 gemm_bf16_kernel(KernelArgs a) {
-  using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N, STAGES, SWZ>;
+  using Cfg = TileCfg<BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ>;
   constexpr int T = Cfg::kThreads;
+  constexpr int CPR = Cfg::kCpr;
+  constexpr int LPS = Cfg::kLoadsPerStage;
+  constexpr int LA = Cfg::kLoadsA;
+  static_assert(PIPE != 2, "PIPE 2 is the ping-pong kernel");
   constexpr bool kF32 = (FLAGS & kOutF32) != 0;
   constexpr bool kSplit = (FLAGS & kSplitK) != 0;
   constexpr bool kRagged = (FLAGS & kRaggedK) != 0;
@@ -331,7 +438,7 @@ gemm_bf16_kernel(KernelArgs a) {
   const int kt_begin = split * a.k_tiles_per_split;
   const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
   const int n_iter = kt_end - kt_begin;
-  const int full_tiles = a.K / kBK;  // k-tiles that need no K check
+  const int full_tiles = a.K / BK;  // K-steps that need no K check
 
   // ---- buffer resources: tile-origin based, range = valid rows ----------
   const int rows_a = min(BM, a.M - m0);
@@ -340,19 +447,19 @@ gemm_bf16_kernel(KernelArgs a) {
   const u32x4 rsrc_b = make_rsrc(a.B + (int64_t)n0 * a.ldb, (uint32_t)(rows_b * a.ldb * 2));
 
   // Per-lane load offsets.  Load i of this lane fills LDS slot
-  // s = i*T + tid (16 B each): row s/8, position s%8, which holds logical
-  // chunk (position ^ swz(row)) of that row.
+  // s = i*T + tid (16 B each): row s/CPR, position s%CPR, which holds
+  // logical chunk (position ^ swz(row)) of that row.
   uint32_t voff_a[Cfg::kLoadsA], voff_b[Cfg::kLoadsB];
   int chunk_a[Cfg::kLoadsA], chunk_b[Cfg::kLoadsB];
 #pragma unroll
   for (int i = 0; i < Cfg::kLoadsA; ++i) {
-    const int s = i * T + tid, row = s >> 3, c = (s & 7) ^ swz<SWZ>(row);
+    const int s = i * T + tid, row = s / CPR, c = (s % CPR) ^ swz<SWZ, CPR>(row);
     chunk_a[i] = c;
     voff_a[i] = row < rows_a ? (uint32_t)(row * a.lda * 2 + c * 16) : kOOB;
   }
 #pragma unroll
   for (int i = 0; i < Cfg::kLoadsB; ++i) {
-    const int s = i * T + tid, row = s >> 3, c = (s & 7) ^ swz<SWZ>(row);
+    const int s = i * T + tid, row = s / CPR, c = (s % CPR) ^ swz<SWZ, CPR>(row);
     chunk_b[i] = c;
     voff_b[i] = row < rows_b ? (uint32_t)(row * a.ldb * 2 + c * 16) : kOOB;
   }
@@ -361,13 +468,32 @@ gemm_bf16_kernel(KernelArgs a) {
     const int kt = kt_begin + it;
     const uint32_t base = smem_addr + (it % STAGES) * Cfg::kStageBytes;
     if (kt < full_tiles) {
-      issue_tile_loads<Cfg::kLoadsA, T>(rsrc_a, base, voff_a, kt * kBK, wave);
-      issue_tile_loads<Cfg::kLoadsB, T>(rsrc_b, base + Cfg::kABytes, voff_b, kt * kBK, wave);
+      issue_tile_loads<Cfg::kLoadsA, T>(rsrc_a, base, voff_a, kt * BK, wave);
+      issue_tile_loads<Cfg::kLoadsB, T>(rsrc_b, base + Cfg::kABytes, voff_b, kt * BK, wave);
     } else {
-      issue_tail_loads<Cfg::kLoadsA, T>(rsrc_a, base, voff_a, chunk_a, kt * kBK, a.K, wave);
-      issue_tail_loads<Cfg::kLoadsB, T>(rsrc_b, base + Cfg::kABytes, voff_b, chunk_b, kt * kBK,
+      issue_tail_loads<Cfg::kLoadsA, T>(rsrc_a, base, voff_a, chunk_a, kt * BK, a.K, wave);
+      issue_tail_loads<Cfg::kLoadsB, T>(rsrc_b, base + Cfg::kABytes, voff_b, chunk_b, kt * BK,
                                         a.K, wave);
     }
+  };
+
+  // Wait until step `it` has landed in every wave and publish it.  Steps
+  // issued so far: 0 .. it+STAGES-2 (it >= 1; the refill of slot it-1
+  // happens after this wait), or 0 .. STAGES-1 for it == 0 (the prologue),
+  // so STAGES-2 (or STAGES-1) later steps' loads may stay in flight, fewer
+  // near the end of the range.  A ragged K's last step is patched first.
+  auto wait_step = [&](int it) {
+    if constexpr (kRagged) {
+      if (kt_begin + it == a.k_tiles - 1) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_u8* st = smem + (it % STAGES) * Cfg::kStageBytes;
+        fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, (kt_begin + it) * BK, a.K, tid);
+        fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, (kt_begin + it) * BK, a.K,
+                                         tid);
+      }
+    }
+    const int later = min(it == 0 ? STAGES - 1 : STAGES - 2, n_iter - 1 - it);
+    ring_wait_barrier_n<LPS, STAGES - 1>(later);
   };
 
   f32x16 acc[Cfg::kFragM][Cfg::kFragN];
@@ -378,111 +504,162 @@ gemm_bf16_kernel(KernelArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // ---- prologue: fill STAGES-1 slots ------------------------------------
-#pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < n_iter) issue_stage(p);
+  constexpr int kReads = Cfg::kFragM + Cfg::kFragN;
+  constexpr int kMfmas = Cfg::kFragM * Cfg::kFragN;
+  bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
 
-  // ---- main loop ----------------------------------------------------------
-  for (int it = 0; it < n_iter; ++it) {
-    lds_u8* stage = smem + (it % STAGES) * Cfg::kStageBytes;
-    if constexpr (kRagged) {
-      if (kt_begin + it == a.k_tiles - 1) {
-        // The last K-step: wait for all of this wave's loads, zero the part
-        // of the chunk that straddles K, then publish with the barrier below.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        fix_tail_chunks<Cfg::kLoadsA, T>(stage, chunk_a, (kt_begin + it) * kBK, a.K, tid);
-        fix_tail_chunks<Cfg::kLoadsB, T>(stage + Cfg::kABytes, chunk_b, (kt_begin + it) * kBK,
-                                         a.K, tid);
+  if constexpr (PIPE == 0) {
+    if (n_iter > 0) {
+      // ---- prologue: every slot gets a K-step in flight -------------------
+#pragma unroll
+      for (int p = 0; p < STAGES; ++p)
+        if (p < n_iter) issue_stage(p);
+      wait_step(0);
+      read_frags<Cfg, SWZ>(smem, smem + Cfg::kABytes, 0, wm, wn, lane, fa[0], fb[0]);
+
+      // ---- main loop --------------------------------------------------------
+      // Substep j of step `it` uses fragment buffer (it*kSub + j) & 1.
+      for (int it = 0; it < n_iter; ++it) {
+        const lds_u8* sa = smem + (it % STAGES) * Cfg::kStageBytes;
+        const lds_u8* sb = sa + Cfg::kABytes;
+        const int b0 = (it * Cfg::kSub) & 1;
+#pragma unroll
+        for (int kk = 0; kk + 1 < Cfg::kSub; ++kk) {
+          const int cur = (b0 + kk) & 1, nxt = cur ^ 1;
+          read_frags<Cfg, SWZ>(sa, sb, kk + 1, wm, wn, lane, fa[nxt], fb[nxt]);
+          __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // DS reads
+          mfma_block<Cfg>(acc, fa[cur], fb[cur]);
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);  // MFMAs
+        }
+        const int cur = (b0 + Cfg::kSub - 1) & 1, nxt = cur ^ 1;
+        if (it + 1 < n_iter) {
+          // Every wave now holds step it's last fragments (lgkmcnt(0) inside
+          // the wait), so slot it % STAGES is free: refill it with step
+          // it+STAGES and start reading step it+1 under the last MFMAs.
+          wait_step(it + 1);
+          if (it + STAGES < n_iter) issue_stage(it + STAGES);
+          const lds_u8* na = smem + ((it + 1) % STAGES) * Cfg::kStageBytes;
+          read_frags<Cfg, SWZ>(na, na + Cfg::kABytes, 0, wm, wn, lane, fa[nxt], fb[nxt]);
+          __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+        }
+        mfma_block<Cfg>(acc, fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
       }
     }
-    // This wave's loads for step `it` have landed once at most the later
-    // steps' loads remain outstanding; its LDS accesses of the previous step
-    // are done.  After the barrier the same holds for every wave, so slot
-    // (it-1) % STAGES may be refilled.
-    if (it + STAGES - 2 < n_iter) ring_wait_barrier<Cfg::kLoadsPerStage * (STAGES - 2)>();
-    else ring_wait_barrier<0>();
-    if (it + STAGES - 1 < n_iter) issue_stage(it + STAGES - 1);
+  } else {
+    // ---- spread issue -------------------------------------------------------
+    // The loads of step X form kSub groups of G.  Group 0 is issued right
+    // after the barrier that frees slot X % STAGES (in the middle of step
+    // X-STAGES), groups 1..kSub-1 during the first kSub-1 substeps of step
+    // X-STAGES+1, each load between two MFMAs.  Steps past the end of the
+    // range are not issued, and the wait counts shrink to match.
+    // Window substep w (0 = the last substep of the step in which the
+    // barrier freed the slot, 1..kSub-1 = the next step's first substeps)
+    // issues loads [lo(w), lo(w+1)) of the step being loaded.
+    constexpr int F = PIPE == 1 ? Cfg::kSub : PIPE == 3 ? Cfg::kSub - 1 : Cfg::kSub - 2;
+    static_assert(F >= 1 && F <= Cfg::kSub, "issue window");
+    static_assert(LPS <= F * kMfmas, "at most one load per MFMA");
+    constexpr int G0 = LPS / F;  // loads in window substep 0
 
-    const lds_u8* sa = stage;
-    const lds_u8* sb = stage + Cfg::kABytes;
-    // Fragments are double-buffered across the four 16-wide substeps: the
-    // reads for substep kk+1 are issued ahead of substep kk's MFMAs.
-    constexpr int kReads = Cfg::kFragM + Cfg::kFragN;
-    constexpr int kMfmas = Cfg::kFragM * Cfg::kFragN;
-    bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
-    read_frags<Cfg, SWZ>(sa, sb, 0, wm, wn, lane, fa[0], fb[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // DS reads
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      if (kk + 1 < kBK / 16) {
-        read_frags<Cfg, SWZ>(sa, sb, kk + 1, wm, wn, lane, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    // Load i (0..LPS-1; A loads first) of step `it`, if that step exists.
+    auto dma_one = [&](int it, int i) {
+      if (it >= n_iter) return;
+      const int kt = kt_begin + it;
+      const int k0 = kt * BK;
+      const bool fast = kt < full_tiles;
+      const int klim = a.K;
+      const uint32_t base = smem_addr + (it % STAGES) * Cfg::kStageBytes;
+      uint32_t dst, vbase;
+      int chunk;
+      if (i < LA) {
+        dst = base + (i * T + wave * 64) * 16;
+        vbase = voff_a[i];
+        chunk = chunk_a[i];
+      } else {
+        dst = base + Cfg::kABytes + ((i - LA) * T + wave * 64) * 16;
+        vbase = voff_b[i - LA];
+        chunk = chunk_b[i - LA];
       }
-      mfma_block<Cfg>(acc, fa[kk & 1], fb[kk & 1]);
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);  // MFMA
+      const uint32_t tailv = (k0 + chunk * 8 < klim) ? vbase + (uint32_t)(k0 * 2) : kOOB;
+      const uint32_t vo = fast ? vbase : tailv;
+      const uint32_t so = fast ? (uint32_t)(k0 * 2) : 0u;
+      dma16(i < LA ? rsrc_a : rsrc_b, dst, vo, so);
+    };
+
+
+    // "Step j has landed", in the middle of step j-1: every load of the
+    // steps j+1 .. min(j+STAGES-2, n_iter-1) is issued and may still be in
+    // flight; none of step j+STAGES-1.
+    auto wait_mid = [&](int j) {
+      if constexpr (kRagged) {
+        if (kt_begin + j == a.k_tiles - 1) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          lds_u8* st = smem + (j % STAGES) * Cfg::kStageBytes;
+          fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, (kt_begin + j) * BK, a.K, tid);
+          fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, (kt_begin + j) * BK, a.K,
+                                           tid);
+        }
+      }
+      ring_wait_barrier_n<LPS, STAGES - 2>(min(STAGES - 2, n_iter - 1 - j));
+    };
+
+    if (n_iter > 0) {
+      // prologue: steps 0..STAGES-2 whole, group 0 of step STAGES-1
+#pragma unroll
+      for (int p = 0; p + 1 < STAGES; ++p)
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) dma_one(p, i);
+#pragma unroll
+      for (int q = 0; q < G0; ++q) dma_one(STAGES - 1, q);
+      if constexpr (kRagged) {
+        if (kt_begin == a.k_tiles - 1) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          fix_tail_chunks<Cfg::kLoadsA, T>(smem, chunk_a, kt_begin * BK, a.K, tid);
+          fix_tail_chunks<Cfg::kLoadsB, T>(smem + Cfg::kABytes, chunk_b, kt_begin * BK, a.K, tid);
+        }
+      }
+      // in flight: steps 1 .. min(STAGES-2, n_iter-1) whole, group 0 of
+      // step STAGES-1 if it exists
+      ring_wait_barrier_ng<LPS, STAGES - 2, G0>(min(STAGES - 2, n_iter - 1), STAGES - 1 < n_iter);
+      read_frags<Cfg, SWZ>(smem, smem + Cfg::kABytes, 0, wm, wn, lane, fa[0], fb[0]);
+
+      for (int it = 0; it < n_iter; ++it) {
+        const lds_u8* sa = smem + (it % STAGES) * Cfg::kStageBytes;
+        const lds_u8* sb = sa + Cfg::kABytes;
+        const int b0 = (it * Cfg::kSub) & 1;
+#pragma unroll
+        for (int kk = 0; kk + 1 < Cfg::kSub; ++kk) {
+          const int cur = (b0 + kk) & 1, nxt = cur ^ 1;
+          read_frags<Cfg, SWZ>(sa, sb, kk + 1, wm, wn, lane, fa[nxt], fb[nxt]);
+          // window substep kk+1 of step it+STAGES-1
+          constexpr_for_window<F, LPS>(kk + 1, [&](auto lo, auto hi) {
+            constexpr int kLo = decltype(lo)::value, kHi = decltype(hi)::value;
+            mfma_block_dma<Cfg, kHi - kLo>(acc, fa[cur], fb[cur],
+                                           [&](int q) { dma_one(it + STAGES - 1, kLo + q); });
+          });
+        }
+        const int cur = (b0 + Cfg::kSub - 1) & 1, nxt = cur ^ 1;
+        if (it + 1 < n_iter) {
+          wait_mid(it + 1);
+          const lds_u8* na = smem + ((it + 1) % STAGES) * Cfg::kStageBytes;
+          read_frags<Cfg, SWZ>(na, na + Cfg::kABytes, 0, wm, wn, lane, fa[nxt], fb[nxt]);
+        }
+        // (no load of step it+STAGES exists in the last step, so nothing is
+        // written into the slot that other waves may still be reading)
+        mfma_block_dma<Cfg, G0>(acc, fa[cur], fb[cur], [&](int q) { dma_one(it + STAGES, q); });
+      }
     }
   }
 
   const int m_base = m0 + wm * Cfg::kWaveM;
   const int n_base = n0 + wn * Cfg::kWaveN;
-
   if constexpr (kSplit) {
-    // ---- split-K: publish the partial; the last arriver reduces ----------
-    // Workspace layout: [tile][slice][q][thread] of float4, q = the lane's
-    // float4 index (fm, fn, g), so every store and load is one contiguous
-    // 16 B per lane.
-    constexpr int Q = Cfg::kFragM * Cfg::kFragN * 4;
-    f32x4* ws = (f32x4*)a.partials + (int64_t)t * a.splits * Q * T;
-    {
-      f32x4* mine = ws + (int64_t)split * Q * T;
-#pragma unroll
-      for (int fm = 0; fm < Cfg::kFragM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < Cfg::kFragN; ++fn)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int q = (fm * Cfg::kFragN + fn) * 4 + g;
-            __builtin_nontemporal_store(
-                (f32x4){acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
-                        acc[fm][fn][4 * g + 3]},
-                mine + q * T + tid);
-          }
-    }
-    // Make this thread's partial visible device-wide before the count.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __shared__ uint32_t s_last;
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev =
-          __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t last = (prev == (uint32_t)a.splits - 1) ? 1u : 0u;
-      // every slice has counted: reset for the next call on this workspace
-      if (last) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // acc = p_0 + p_1 + ... + p_{S-1} in this order, whichever slice is last.
-#pragma unroll
-    for (int fm = 0; fm < Cfg::kFragM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < Cfg::kFragN; ++fn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int q = (fm * Cfg::kFragN + fn) * 4 + g;
-          f32x4 sum = __builtin_nontemporal_load(ws + q * T + tid);
-          for (int sl = 1; sl < a.splits; ++sl)
-            sum += __builtin_nontemporal_load(ws + ((int64_t)sl * Q + q) * T + tid);
-          acc[fm][fn][4 * g] = sum[0];
-          acc[fm][fn][4 * g + 1] = sum[1];
-          acc[fm][fn][4 * g + 2] = sum[2];
-          acc[fm][fn][4 * g + 3] = sum[3];
-        }
+    // slice `split` owns partial buffer `split` (fp32, stride ldc)
+    store_tile<Cfg, true>(a, (float*)a.C + (int64_t)split * a.c_split_stride, acc, m_base,
+                          n_base, lane);
+  } else {
+    store_tile<Cfg, kF32>(a, a.C, acc, m_base, n_base, lane);
   }
-
-  store_tile<Cfg, kF32>(a, acc, m_base, n_base, lane);
 }
 
 }  // namespace gemm

@@ -1,0 +1,62 @@
+// Launcher template for one tile configuration: maps the run-time variant
+// flags (kOutF32 | kSplitK | kRaggedK) to the instantiated kernels.  Each
+// gemm_inst_*.hip file instantiates it for its configurations, so the
+// configurations compile in parallel.
+#pragma once
+
+#include "gemm_kernel.hpp"
+#include "gemm_pingpong.hpp"
+
+namespace gemm {
+
+// PIPE 0 / 1: gemm_bf16_kernel with burst / spread load issue;
+// PIPE 2: gemm_bf16_pingpong_kernel (8 waves as 2 x 4).
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int FLAGS>
+hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
+  if constexpr (PIPE == 2) {
+    static_assert(WM == 2 && WN == 4, "ping-pong runs 2 x 4 waves");
+    hipLaunchKernelGGL((gemm_bf16_pingpong_kernel<BM, BN, BK, ST, SWZ, FLAGS>), dim3(grid),
+                       dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, ST, SWZ, PIPE, FLAGS>), dim3(grid),
+                       dim3(WM * WN * 64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE>
+hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
+  if (flags & kSplitK) flags &= ~kOutF32;  // split slices always write fp32 partials
+  switch (flags & 7) {
+    case 0: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 0>(a, grid, s);
+    case 1: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 1>(a, grid, s);
+    case 2: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 2>(a, grid, s);
+    case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 4>(a, grid, s);
+    case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 5>(a, grid, s);
+    default: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 6>(a, grid, s);
+  }
+}
+
+// Every built configuration:
+//   X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ, PIPE, TU)
+// where TU names the gemm_inst_<TU>.hip file that instantiates it.
+#define GEMM_TILE_CONFIGS(X)                                      \
+  X(t256x256x64_w2x2_s2_x2_p0, 256, 256, 64, 2, 2, 2, 2, 0, a)    \
+  X(t256x256x64_w2x2_s2_x2_p3, 256, 256, 64, 2, 2, 2, 2, 3, b)    \
+  X(t256x256x64_w2x2_s2_x2_p4, 256, 256, 64, 2, 2, 2, 2, 4, c)    \
+  X(t256x256x64_w2x2_s2_x2_p1, 256, 256, 64, 2, 2, 2, 2, 1, d)    \
+  X(t256x256x64_w2x4_s2_x2_p3, 256, 256, 64, 2, 4, 2, 2, 3, e)    \
+  X(t256x256x64_w2x4_s2_x2_p1, 256, 256, 64, 2, 4, 2, 2, 1, f)    \
+  X(t256x256x32_w2x4_s4_x2_p2, 256, 256, 32, 2, 4, 4, 2, 2, g)    \
+  X(t256x128x64_w2x2_s3_x2_p1, 256, 128, 64, 2, 2, 3, 2, 1, h)    \
+  X(t256x128x64_w2x2_s2_x2_p3, 256, 128, 64, 2, 2, 2, 2, 3, k)    \
+  X(t128x128x64_w2x2_s4_x2_p1, 128, 128, 64, 2, 2, 4, 2, 1, i)    \
+  X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, j)    \
+  X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, j)
+
+#define GEMM_DECLARE_LAUNCH(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, TU) \
+  extern template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(const KernelArgs&, int, hipStream_t, int);
+GEMM_TILE_CONFIGS(GEMM_DECLARE_LAUNCH)
+#undef GEMM_DECLARE_LAUNCH
+
+}  // namespace gemm

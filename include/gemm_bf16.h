@@ -33,10 +33,11 @@
  * sum rounded to nearest, ties to even.
  *
  * Ownership.  The caller owns A, B and C; the library neither frees nor
- * retains them.  C must not overlap A or B.  The library owns a split-K
- * workspace per (device, stream): allocated on first need, grown when a
- * larger one is needed (growth synchronises that stream), freed by
- * gemm_bf16_release_workspace.  Pre-size it with gemm_bf16_reserve_workspace
+ * retains them.  C must not overlap A or B.  When a shape's configuration
+ * splits K, the fp32 partial sums of the S slices (S * M * roundup8(N) * 4
+ * bytes) go to a workspace the library owns per (device, stream): allocated
+ * on first need, grown when a larger one is needed (growth synchronises that
+ * stream), freed by gemm_bf16_release_workspace.  Pre-size it with gemm_bf16_reserve_workspace
  * before stream capture, since allocation cannot be captured.
  *
  * Streams and errors.  Calls are asynchronous: work is enqueued on `stream`
@@ -96,9 +97,10 @@ int gemm_bf16_ex(const char* config,
                  void* C, int64_t ldc,
                  int out_f32, void* stream);
 
-/* Name of the configuration gemm_bf16 would choose for this shape (tile
- * sizes, pipeline depth, split count), e.g. "t256x256_s2_k1".  Static
- * storage; never NULL. */
+/* Name of the configuration gemm_bf16 would choose for this shape, e.g.
+ * "t256x256x32_w2x4_s4_x2_p2_k1_g4": tile BM x BN x BK, waves, ring stages,
+ * LDS swizzle, load schedule, then K splits and GROUP_M.  Per-thread static
+ * storage, valid until the thread's next call; never NULL. */
 const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K);
 
 /* Enumerate the built configurations: the i-th name, or NULL past the end. */

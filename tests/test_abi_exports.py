@@ -1,0 +1,105 @@
+"""The C-ABI library loads on a machine without a GPU and exports every
+function ``include/gemm_bf16.h`` declares; host-side logic (argument checks,
+status strings, configuration names and workspace sizes) answers without
+touching a device.  No call here launches work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_bf16.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from dense_gemm_bf16_amd import build as b
+
+    if not os.path.exists(b.LIB):
+        b.build()
+    import dense_gemm_bf16_amd as g
+
+    return g
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(gemm_bf16\w*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["gemm_bf16", "gemm_bf16_f32out", "gemm_bf16_ex", "gemm_bf16_config_name",
+              "gemm_bf16_config_at", "gemm_bf16_status_string", "gemm_bf16_last_hip_error",
+              "gemm_bf16_reserve_workspace", "gemm_bf16_workspace_size",
+              "gemm_bf16_release_workspace"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(so, n), n
+
+
+def test_binding_names_match_header(lib):
+    for n in declared_functions():
+        short = n.replace("gemm_bf16_", "")
+        assert hasattr(lib, n) or hasattr(lib, short), n
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in range(5):
+        s = lib.status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 5
+    assert lib.status_string(99) == "unknown status"
+
+
+def test_argument_checks_need_no_device(lib):
+    so = lib._lib
+    fake = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: checks fail first
+    assert so.gemm_bf16(-1, 8, 8, fake, 8, fake, 8, fake, 8, None) == lib.GEMM_ERR_INVALID_ARG
+    assert so.gemm_bf16(8, 8, 16, fake, 8, fake, 16, fake, 8, None) == lib.GEMM_ERR_INVALID_ARG
+    assert so.gemm_bf16(8, 8, 8, None, 8, fake, 8, fake, 8, None) == lib.GEMM_ERR_INVALID_ARG
+    assert so.gemm_bf16(8, 8, 8, fake, 8, fake, 8, None, 8, None) == lib.GEMM_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(0x10008)
+    assert so.gemm_bf16(8, 8, 8, odd, 8, fake, 8, fake, 8, None) == lib.GEMM_ERR_MISALIGNED
+    assert so.gemm_bf16(8, 8, 12, fake, 12, fake, 16, fake, 8, None) == lib.GEMM_ERR_MISALIGNED
+    assert so.gemm_bf16_ex(b"no_such_config", 8, 8, 8, fake, 8, fake, 8, fake, 8, 0,
+                           None) == lib.GEMM_ERR_UNSUPPORTED
+
+
+def test_config_names(lib):
+    names = lib.config_names()
+    assert len(names) == len(set(names)) >= 2
+    pat = re.compile(r"^t(\d+)x(\d+)x(\d+)_w(\d)x(\d)_s(\d)_x(\d)_p(\d)$")
+    for n in names:
+        assert pat.match(n), n
+    from synthetic_inputs import WORKLOADS
+
+    for w in WORKLOADS.values():
+        chosen = lib.config_name(w.M, w.N, w.K)
+        m = re.match(r"^(.*)_k(\d+)_g(\d+)$", chosen)
+        assert m and m.group(1) in names, chosen
+        S = int(m.group(2))
+        ws = lib.workspace_size(w.M, w.N, w.K)
+        if S == 1:
+            assert ws == 0
+        else:
+            assert ws == S * w.M * ((w.N + 7) // 8 * 8) * 4, (w.name, chosen, ws)
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "dense_gemm_bf16_amd")
+    for dirpath, _, files in os.walk(pkg):
+        if "_build" in dirpath:
+            continue
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".c", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"\boracle\b", text), os.path.join(dirpath, f)

@@ -191,9 +191,11 @@ def test_split_k_matches_unsplit_on_integers():
     M, N, K = 256, 1024, 8192
     A = int_bf16(M, K, seed=600)
     B = int_bf16(N, K, seed=601)
+    import dense_gemm_bf16_amd as g
+
     ref16, _ = _oracle().gemm(A, B)
-    for cfg in ["t256x256_w2x2_s2_x1_k1", "t256x256_w2x2_s2_x1_k8",
-                "t256x256_w2x2_s2_x1_k5"]:
+    tile = g.config_name(M, N, K).split("_k")[0]
+    for cfg in [f"{tile}_k1", f"{tile}_k8", f"{tile}_k5"]:
         got = run_gemm(A, B, config=cfg)
         assert check_bf16(got, ref16, None, K, exact=True)["ok"], cfg
 
