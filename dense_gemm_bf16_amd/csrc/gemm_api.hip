@@ -74,27 +74,33 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 }
 
 // ------------------------------------------------------------ config choice
-// Static shape -> configuration rules, from measurements on MI355X (the
-// sweeps are summarised in the design notes):
-//  * enough 256x256 tiles to fill the 256 CUs (4096^3, M = 8192 prefill):
-//    the eight-wave ping-pong kernel, no split;
-//  * very small M (decode batches up to 64 rows): the same kernel with K
-//    split so that about 256 workgroups stream B;
-//  * otherwise (M of a few hundred, e.g. the M = 256 decode layers and the
-//    512-row projection): 128x128 tiles, K split until about 256 workgroups.
+// Static shape -> configuration rules, from sweeps on MI355X (HIP events,
+// cold B for the memory-bound shapes):
+//  * M <= 64 (small decode batches): 32 x 128 tiles with a six-slot LDS
+//    ring, K split so that about 256 workgroups stream B,
+//    K-step rotation on (the operands' power-of-two row strides otherwise
+//    send concurrent workgroups to the same memory channels: +10-28 %);
+//  * enough 256 x 256 tiles to fill the chip: the eight-wave ping-pong
+//    kernel for about one wave of tiles (4096^3), the register-staged
+//    256 x 256 x 64 kernel for several waves (M = 8192 prefill), no split;
+//  * otherwise (M of a few hundred: the M = 256 decode layers, 512-row
+//    projections): register-staged 256 x 128 tiles, K split to about 256
+//    workgroups, rotation on.
 constexpr int kCUs = 256;
-constexpr const char* kBigTile = "t256x256x32_w2x4_s4_x2_p2";
-constexpr const char* kMidTile = "t128x128x64_w2x2_s4_x2_p1";
+constexpr const char* kPingPong = "t256x256x32_w2x4_s4_x2_p2";
+constexpr const char* kRegStageBig = "t256x256x64_w2x2_s2_x2_p6";
+constexpr const char* kRegStageMid = "t256x128x64_w2x2_s2_x2_p6";
+constexpr const char* kSkinny = "t32x128x64_w1x4_s6_x2_p0";
 
 int64_t tiles_of(const TileConfig* t, int64_t M, int64_t N) {
   return ((M + t->bm - 1) / t->bm) * ((N + t->bn - 1) / t->bn);
 }
 
-// Splits so that tiles * splits is about the CU count, keeping at least 8
-// K-steps per slice.
-int choose_splits(int64_t tiles, int64_t k_tiles) {
-  if (tiles >= kCUs) return 1;
-  int s = (int)((kCUs + tiles / 2) / tiles);
+// Splits so that tiles * splits is about `target` workgroups, keeping at
+// least 8 K-steps per slice.
+int choose_splits(int64_t tiles, int64_t k_tiles, int64_t target = kCUs) {
+  if (tiles <= 0 || tiles >= target) return 1;  // tiles == 0: empty M or N
+  int s = (int)((target + tiles / 2) / tiles);
   while (s > 1 && k_tiles / s < 8) --s;
   return s < 1 ? 1 : s;
 }
@@ -111,32 +117,42 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
     const int64_t per = (k_tiles + p->splits - 1) / p->splits;
     p->splits = (int)((k_tiles + per - 1) / per);
   }
-  snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
+  if (p->k_rot > 0)
+    snprintf(p->name, sizeof p->name, "%s_k%d_g%d_r%d", p->tile->name, p->splits, p->group_m,
+             p->k_rot);
+  else
+    snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
 }
 
 Plan choose_plan(int64_t M, int64_t N, int64_t K) {
   Plan p{};
-  const TileConfig* big = find_tile_config(kBigTile);
-  const TileConfig* mid = find_tile_config(kMidTile);
-  const int64_t big_tiles = tiles_of(big, M, N);
-  if (big_tiles >= kCUs - kCUs / 8 || M <= 64) {
-    p.tile = big;
-    p.splits = choose_splits(big_tiles, (K + big->bk - 1) / big->bk);
-  } else {
-    p.tile = mid;
-    p.splits = choose_splits(tiles_of(mid, M, N), (K + mid->bk - 1) / mid->bk);
-  }
   p.group_m = 4;
+  const TileConfig* big = find_tile_config(kPingPong);
+  const int64_t big_tiles = tiles_of(big, M, N);
+  if (M <= 64) {
+    p.tile = find_tile_config(kSkinny);
+    p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
+    p.k_rot = 1;
+  } else if (big_tiles >= kCUs - kCUs / 8) {
+    p.tile = big_tiles >= 2 * kCUs ? find_tile_config(kRegStageBig) : big;
+    p.splits = 1;
+    p.k_rot = 0;
+  } else {
+    p.tile = find_tile_config(kRegStageMid);
+    p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
+    p.k_rot = 1;
+  }
   finish_plan(&p, M, N, K);
   return p;
 }
 
-// Parse "tile[_k<splits>][_g<group>]" where tile is a table name.
+// Parse "tile[_k<splits>][_g<group>][_r<rotation>]" where tile is a table
+// name.
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out) {
   char buf[64];
   if (strlen(name) >= sizeof buf) return false;
   strcpy(buf, name);
-  int splits = 1, group = 4;
+  int splits = 1, group = 4, rot = 0;
   for (;;) {
     char* u = strrchr(buf, '_');
     if (!u) break;
@@ -147,6 +163,9 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
     } else if (u[1] == 'g' && sscanf(u + 2, "%d", &v) == 1 && v >= 1) {
       group = v;
       *u = 0;
+    } else if (u[1] == 'r' && sscanf(u + 2, "%d", &v) == 1 && v >= 0) {
+      rot = v;
+      *u = 0;
     } else {
       break;
     }
@@ -156,6 +175,7 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
   out->tile = t;
   out->splits = splits;
   out->group_m = group;
+  out->k_rot = rot;
   finish_plan(out, M, N, K);
   return true;
 }
@@ -180,7 +200,10 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   const TileConfig& t = *p.tile;
   // 32-bit limits: tile-relative byte offsets of the operands, grid size,
   // and the int32 shape fields of the kernel.
-  if ((int64_t)t.bm * lda * 2 >= (int64_t(1) << 31) || (int64_t)t.bn * ldb * 2 >= (int64_t(1) << 31))
+  // (a tile's operand range plus the 4 KB a load may move its resource base
+  // back by must stay below 2^31, the voffset that marks an absent chunk)
+  constexpr int64_t kRangeLimit = (int64_t(1) << 31) - 4096;
+  if ((int64_t)t.bm * lda * 2 >= kRangeLimit || (int64_t)t.bn * ldb * 2 >= kRangeLimit)
     return GEMM_ERR_UNSUPPORTED;
   if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31))
     return GEMM_ERR_UNSUPPORTED;
@@ -205,6 +228,7 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   a.splits = p.splits;
   a.k_tiles_per_split = (int32_t)((k_tiles + p.splits - 1) / p.splits);
   a.group_m = p.group_m;
+  a.k_rot = p.k_rot;
   int flags = out_f32 ? kOutF32 : 0;
   if ((K & 7) != 0) flags |= kRaggedK;
   void* ws = nullptr;

@@ -1,0 +1,79 @@
+// Body of every gemm_inst_<tu>.hip file: instantiates launch_cfg for the
+// configurations of GEMM_TILE_CONFIGS whose TU tag is this file's.  The
+// including file defines GEMM_INST_<tu> as GEMM_DO_INST before including
+// this header; every other tag expands to nothing.
+#pragma once
+
+#include "gemm_launch.hpp"
+
+#define GEMM_DO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE) \
+  template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(const KernelArgs&, int, hipStream_t, int);
+#define GEMM_NO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE)
+
+#ifndef GEMM_INST_a
+#define GEMM_INST_a GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_b
+#define GEMM_INST_b GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_c
+#define GEMM_INST_c GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_d
+#define GEMM_INST_d GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_e
+#define GEMM_INST_e GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_f
+#define GEMM_INST_f GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_g
+#define GEMM_INST_g GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_h
+#define GEMM_INST_h GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_i
+#define GEMM_INST_i GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_j
+#define GEMM_INST_j GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_k
+#define GEMM_INST_k GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_l
+#define GEMM_INST_l GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_m
+#define GEMM_INST_m GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_n
+#define GEMM_INST_n GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_o
+#define GEMM_INST_o GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_p
+#define GEMM_INST_p GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_q
+#define GEMM_INST_q GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_r
+#define GEMM_INST_r GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_s
+#define GEMM_INST_s GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_t
+#define GEMM_INST_t GEMM_NO_INST
+#endif
+
+namespace gemm {
+#define GEMM_INSTANTIATE(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, TU) \
+  GEMM_INST_##TU(BM, BN, BK, WM, WN, ST, SWZ, PIPE)
+GEMM_TILE_CONFIGS(GEMM_INSTANTIATE)
+#undef GEMM_INSTANTIATE
+}  // namespace gemm

@@ -31,6 +31,7 @@ struct Plan {
   const TileConfig* tile;
   int splits;
   int group_m;
+  int k_rot;  // K-step rotation stride per tile, 0 = none
   char name[64];
 };
 

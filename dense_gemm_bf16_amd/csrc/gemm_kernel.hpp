@@ -85,6 +85,25 @@ struct KernelArgs {
   int32_t splits;             // slices of K per tile (>= 1)
   int32_t k_tiles_per_split;  // every slice non-empty (host guarantees)
   int32_t group_m;            // raster group height in tiles
+  int32_t k_rot;              // K-step rotation stride per tile (0: none)
+};
+
+// Order of a workgroup's K-steps.  With rotation, the workgroup of tile t
+// starts its K range at step (t * k_rot) mod n instead of 0 and wraps
+// around, so that workgroups running at the same time read different
+// K columns of the operands.  Rows of a power-of-two leading dimension would
+// otherwise send them all to the same few memory channels.  Each workgroup
+// still sums its steps in one fixed order, so results stay reproducible.
+struct KOrder {
+  int begin, n, rot;
+  __device__ KOrder(const KernelArgs& a, int t, int kt_begin, int n_iter)
+      : begin(kt_begin), n(n_iter),
+        rot(a.k_rot > 0 && n_iter > 0 ? (int)(((int64_t)t * a.k_rot) % n_iter) : 0) {}
+  // global K-step of the workgroup's it-th step (0 <= it < n)
+  __device__ __forceinline__ int kt(int it) const {
+    const int j = it + rot;
+    return begin + (j >= n ? j - n : j);
+  }
 };
 
 // Variant flags of the kernel template.
@@ -156,6 +175,32 @@ __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds_addr, uint
       : "memory");
 }
 
+// LDS-DMA load with an instruction offset OFF (< 4096): 16 bytes per lane
+// from rsrc.base + soff + voff + OFF into LDS at M0 + OFF + 16*lane.  The
+// offset steps the LDS destination without rewriting M0, so consecutive
+// loads that share M0 issue faster; `rsrc` must have its base moved back
+// by OFF (see shifted_rsrc) so that the global address stays base + voff.
+template <int OFF>
+__device__ __forceinline__ void dma16_off(const u32x4& rsrc, uint32_t m0, uint32_t voff,
+                                          uint32_t soff) {
+  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds" ::"{m0}"(m0),
+      "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF)
+      : "memory");
+}
+
+// Buffer resource for dma16_off<back>: base moved back by `back` bytes and
+// the range extended by as much, so voffset v addresses base + v and is in
+// range exactly when v < num_bytes, whether or not the hardware counts the
+// instruction offset in its range check.  (The host keeps num_bytes + back
+// below 2^31, so kOOB stays out of range.)
+__device__ __forceinline__ u32x4 shifted_rsrc(const void* base, uint32_t num_bytes,
+                                              uint32_t back) {
+  return make_rsrc((const uint8_t*)base - back, num_bytes + back);
+}
+
 // Workgroup ids are dispatched round-robin over the 8 XCDs.  Remap so that
 // XCD x handles logical ids [start_x, start_x + count_x), contiguous.
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
@@ -173,7 +218,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 //          pairs.  128-byte rows: (row ^ row/8) mod 8; 64-byte rows:
 //          (row / 4) mod 4.
 template <int SWZ, int CPR>
-__device__ __forceinline__ int swz(int row) {
+__host__ __device__ constexpr int swz(int row) {
   if constexpr (SWZ == 0) return 0;
   else if constexpr (SWZ == 1) return row & (CPR - 1);
   else if constexpr (CPR == 8) return (row ^ (row >> 3)) & 7;
@@ -294,6 +339,22 @@ __device__ __forceinline__ void mfma_block(f32x16 (&acc)[Cfg::kFragM][Cfg::kFrag
 #pragma unroll
     for (int fn = 0; fn < Cfg::kFragN; ++fn)
       acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+}
+
+// Call f(std::integral_constant<int, i>) for i = 0 .. N-1 in order.
+template <int I, int N>
+struct ConstexprFor {
+  template <typename Fn>
+  __device__ __forceinline__ static void run(Fn&& f) {
+    if constexpr (I < N) {
+      f(std::integral_constant<int, I>{});
+      ConstexprFor<I + 1, N>::run(f);
+    }
+  }
+};
+template <int N, typename Fn>
+__device__ __forceinline__ void constexpr_for(Fn&& f) {
+  ConstexprFor<0, N>::run(f);
 }
 
 // Call f(lo, hi) with compile-time integral constants lo = w*L/F and
@@ -438,6 +499,7 @@ gemm_bf16_kernel(KernelArgs a) {
   const int kt_begin = split * a.k_tiles_per_split;
   const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
   const int n_iter = kt_end - kt_begin;
+  const KOrder korder(a, t, kt_begin, n_iter);
   const int full_tiles = a.K / BK;  // K-steps that need no K check
 
   // ---- buffer resources: tile-origin based, range = valid rows ----------
@@ -465,7 +527,7 @@ gemm_bf16_kernel(KernelArgs a) {
   }
 
   auto issue_stage = [&](int it) {
-    const int kt = kt_begin + it;
+    const int kt = korder.kt(it);
     const uint32_t base = smem_addr + (it % STAGES) * Cfg::kStageBytes;
     if (kt < full_tiles) {
       issue_tile_loads<Cfg::kLoadsA, T>(rsrc_a, base, voff_a, kt * BK, wave);
@@ -484,11 +546,11 @@ gemm_bf16_kernel(KernelArgs a) {
   // near the end of the range.  A ragged K's last step is patched first.
   auto wait_step = [&](int it) {
     if constexpr (kRagged) {
-      if (kt_begin + it == a.k_tiles - 1) {
+      if (korder.kt(it) == a.k_tiles - 1) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_u8* st = smem + (it % STAGES) * Cfg::kStageBytes;
-        fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, (kt_begin + it) * BK, a.K, tid);
-        fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, (kt_begin + it) * BK, a.K,
+        fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, korder.kt(it) * BK, a.K, tid);
+        fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, korder.kt(it) * BK, a.K,
                                          tid);
       }
     }
@@ -564,7 +626,7 @@ gemm_bf16_kernel(KernelArgs a) {
     // Load i (0..LPS-1; A loads first) of step `it`, if that step exists.
     auto dma_one = [&](int it, int i) {
       if (it >= n_iter) return;
-      const int kt = kt_begin + it;
+      const int kt = korder.kt(it);
       const int k0 = kt * BK;
       const bool fast = kt < full_tiles;
       const int klim = a.K;
@@ -592,11 +654,11 @@ gemm_bf16_kernel(KernelArgs a) {
     // flight; none of step j+STAGES-1.
     auto wait_mid = [&](int j) {
       if constexpr (kRagged) {
-        if (kt_begin + j == a.k_tiles - 1) {
+        if (korder.kt(j) == a.k_tiles - 1) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           lds_u8* st = smem + (j % STAGES) * Cfg::kStageBytes;
-          fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, (kt_begin + j) * BK, a.K, tid);
-          fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, (kt_begin + j) * BK, a.K,
+          fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, korder.kt(j) * BK, a.K, tid);
+          fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, korder.kt(j) * BK, a.K,
                                            tid);
         }
       }
@@ -612,10 +674,10 @@ gemm_bf16_kernel(KernelArgs a) {
 #pragma unroll
       for (int q = 0; q < G0; ++q) dma_one(STAGES - 1, q);
       if constexpr (kRagged) {
-        if (kt_begin == a.k_tiles - 1) {
+        if (korder.kt(0) == a.k_tiles - 1) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          fix_tail_chunks<Cfg::kLoadsA, T>(smem, chunk_a, kt_begin * BK, a.K, tid);
-          fix_tail_chunks<Cfg::kLoadsB, T>(smem + Cfg::kABytes, chunk_b, kt_begin * BK, a.K, tid);
+          fix_tail_chunks<Cfg::kLoadsA, T>(smem, chunk_a, korder.kt(0) * BK, a.K, tid);
+          fix_tail_chunks<Cfg::kLoadsB, T>(smem + Cfg::kABytes, chunk_b, korder.kt(0) * BK, a.K, tid);
         }
       }
       // in flight: steps 1 .. min(STAGES-2, n_iter-1) whole, group 0 of

@@ -6,22 +6,35 @@
 
 #include "gemm_kernel.hpp"
 #include "gemm_pingpong.hpp"
+#include "gemm_regstage.hpp"
 
 namespace gemm {
 
-// PIPE 0 / 1: gemm_bf16_kernel with burst / spread load issue;
-// PIPE 2: gemm_bf16_pingpong_kernel (8 waves as 2 x 4).
+// PIPE 0 / 1 / 3 / 4: gemm_bf16_kernel with burst / spread load issue;
+// PIPE 2 / 5: gemm_bf16_pingpong_kernel (8 waves as 2 x 4) with the
+// thread-strided / wave-contiguous dealing of loads;
+// PIPE 6: gemm_bf16_regstage_kernel (loads staged through ST register
+// buffers, two LDS slots).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int FLAGS>
 hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
-  if constexpr (PIPE == 2) {
+  if constexpr (PIPE == 2 || PIPE == 5) {
     static_assert(WM == 2 && WN == 4, "ping-pong runs 2 x 4 waves");
-    hipLaunchKernelGGL((gemm_bf16_pingpong_kernel<BM, BN, BK, ST, SWZ, FLAGS>), dim3(grid),
-                       dim3(512), 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_pingpong_kernel<BM, BN, BK, ST, SWZ, FLAGS, PIPE == 5>),
+                       dim3(grid), dim3(512), 0, s, a);
+  } else if constexpr (PIPE == 6) {
+    hipLaunchKernelGGL((gemm_bf16_regstage_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS>),
+                       dim3(grid), dim3(WM * WN * 64), 0, s, a);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, ST, SWZ, PIPE, FLAGS>), dim3(grid),
                        dim3(WM * WN * 64), 0, s, a);
   }
   return hipGetLastError();
+}
+
+// LDS bytes a configuration's kernel allocates.
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE>
+constexpr int lds_bytes_of() {
+  return TileCfg<BM, BN, BK, WM, WN, PIPE == 6 ? 2 : ST, SWZ>::kLdsBytes;
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE>
@@ -48,9 +61,21 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t256x256x64_w2x4_s2_x2_p3, 256, 256, 64, 2, 4, 2, 2, 3, e)    \
   X(t256x256x64_w2x4_s2_x2_p1, 256, 256, 64, 2, 4, 2, 2, 1, f)    \
   X(t256x256x32_w2x4_s4_x2_p2, 256, 256, 32, 2, 4, 4, 2, 2, g)    \
+  X(t256x256x32_w2x4_s4_x2_p5, 256, 256, 32, 2, 4, 4, 2, 5, l)    \
+  X(t256x256x32_w2x2_s3_x2_p6, 256, 256, 32, 2, 2, 3, 2, 6, m)    \
+  X(t256x256x32_w2x2_s4_x2_p6, 256, 256, 32, 2, 2, 4, 2, 6, n)    \
+  X(t256x256x64_w2x2_s2_x2_p6, 256, 256, 64, 2, 2, 2, 2, 6, o)    \
   X(t256x128x64_w2x2_s3_x2_p1, 256, 128, 64, 2, 2, 3, 2, 1, h)    \
   X(t256x128x64_w2x2_s2_x2_p3, 256, 128, 64, 2, 2, 2, 2, 3, k)    \
   X(t128x128x64_w2x2_s4_x2_p1, 128, 128, 64, 2, 2, 4, 2, 1, i)    \
+  X(t64x256x64_w1x4_s4_x2_p0, 64, 256, 64, 1, 4, 4, 2, 0, p)      \
+  X(t32x256x64_w1x4_s4_x2_p0, 32, 256, 64, 1, 4, 4, 2, 0, p)      \
+  X(t64x128x64_w1x4_s6_x2_p0, 64, 128, 64, 1, 4, 6, 2, 0, q)      \
+  X(t32x128x64_w1x4_s6_x2_p0, 32, 128, 64, 1, 4, 6, 2, 0, q)      \
+  X(t64x256x64_w1x4_s4_x2_p6, 64, 256, 64, 1, 4, 4, 2, 6, r)      \
+  X(t32x256x64_w1x4_s4_x2_p6, 32, 256, 64, 1, 4, 4, 2, 6, r)      \
+  X(t256x128x64_w2x2_s2_x2_p6, 256, 128, 64, 2, 2, 2, 2, 6, s)    \
+  X(t128x256x64_w2x2_s2_x2_p6, 128, 256, 64, 2, 2, 2, 2, 6, s)    \
   X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, j)    \
   X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, j)
 

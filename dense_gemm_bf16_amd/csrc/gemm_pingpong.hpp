@@ -41,7 +41,14 @@
 
 namespace gemm {
 
-template <int BM, int BN, int BK, int STAGES, int SWZ, int FLAGS>
+// CONTIG selects how a step's LDS-DMA loads are dealt to the waves:
+//   false: load i of thread t fills the 16-byte LDS slot i*512 + t, so a
+//          wave's loads are 8 KB apart and each rewrites M0;
+//   true:  the step's 1 KB loads are numbered through the stage (A's
+//          first), and wave w issues loads w*L .. w*L+L-1 (L per wave): they
+//          are adjacent in LDS, so up to four share one M0 value and differ
+//          only in the instruction offset, which lets them issue faster.
+template <int BM, int BN, int BK, int STAGES, int SWZ, int FLAGS, bool CONTIG>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 gemm_bf16_pingpong_kernel(KernelArgs a) {
   using Cfg = TileCfg<BM, BN, BK, 2, 4, STAGES, SWZ>;
@@ -83,6 +90,7 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   const int kt_begin = split * a.k_tiles_per_split;
   const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
   const int n_iter = kt_end - kt_begin;
+  const KOrder korder(a, t, kt_begin, n_iter);
   const int full_tiles = a.K / BK;
 
   const int rows_a = min(BM, a.M - m0);
@@ -92,25 +100,67 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
 
   uint32_t voff_a[Cfg::kLoadsA], voff_b[Cfg::kLoadsB];
   int chunk_a[Cfg::kLoadsA], chunk_b[Cfg::kLoadsB];
+  // wave-contiguous dealing: load i of this wave is stage load g = wave*LPS + i
+  constexpr int kStageLoadsA = Cfg::kABytes / 1024;
+  static_assert(Cfg::kABytes % 1024 == 0 && 8 * LPS * 1024 == Cfg::kStageBytes,
+                "a step is 8 waves x LPS loads of 1 KB, A's first");
+  uint32_t voff_c[LPS];
+  int chunk_c[LPS];
+  u32x4 rsrc_c[LPS];
+  if constexpr (CONTIG) {
 #pragma unroll
-  for (int i = 0; i < Cfg::kLoadsA; ++i) {
-    const int s = i * T + tid, row = s / CPR, c = (s % CPR) ^ swz<SWZ, CPR>(row);
-    chunk_a[i] = c;
-    voff_a[i] = row < rows_a ? (uint32_t)(row * a.lda * 2 + c * 16) : kOOB;
-  }
+    for (int i = 0; i < LPS; ++i) {
+      const int g = wave * LPS + i;
+      const bool is_a = g < kStageLoadsA;
+      const int s = (is_a ? g : g - kStageLoadsA) * 64 + lane;
+      const int row = s / CPR, c = (s % CPR) ^ swz<SWZ, CPR>(row);
+      chunk_c[i] = c;
+      const int rows = is_a ? rows_a : rows_b;
+      const int ld = is_a ? a.lda : a.ldb;
+      voff_c[i] = row < rows ? (uint32_t)(row * ld * 2 + c * 16) : kOOB;
+      const uint32_t back = (uint32_t)((i % 4) * 1024);
+      rsrc_c[i] = is_a ? shifted_rsrc(a.A + (int64_t)m0 * a.lda, (uint32_t)(rows_a * a.lda * 2), back)
+                       : shifted_rsrc(a.B + (int64_t)n0 * a.ldb, (uint32_t)(rows_b * a.ldb * 2), back);
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < Cfg::kLoadsB; ++i) {
-    const int s = i * T + tid, row = s / CPR, c = (s % CPR) ^ swz<SWZ, CPR>(row);
-    chunk_b[i] = c;
-    voff_b[i] = row < rows_b ? (uint32_t)(row * a.ldb * 2 + c * 16) : kOOB;
+    for (int i = 0; i < Cfg::kLoadsA; ++i) {
+      const int s = i * T + tid, row = s / CPR, c = (s % CPR) ^ swz<SWZ, CPR>(row);
+      chunk_a[i] = c;
+      voff_a[i] = row < rows_a ? (uint32_t)(row * a.lda * 2 + c * 16) : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::kLoadsB; ++i) {
+      const int s = i * T + tid, row = s / CPR, c = (s % CPR) ^ swz<SWZ, CPR>(row);
+      chunk_b[i] = c;
+      voff_b[i] = row < rows_b ? (uint32_t)(row * a.ldb * 2 + c * 16) : kOOB;
+    }
   }
 
   // This wave's loads of step `it` (nothing if the step does not exist).
   auto issue_step = [&](int it) {
     if (it >= n_iter) return;
-    const int kt = kt_begin + it;
+    const int kt = korder.kt(it);
     const uint32_t base = smem_addr + (it % STAGES) * Cfg::kStageBytes;
-    if (kt < full_tiles) {
+    if constexpr (CONTIG) {
+      const uint32_t wbase = base + wave * LPS * 1024;
+      const int k0 = kt * BK;
+      if (kt < full_tiles) {
+        // K offset in soffset: the per-lane offsets are used as they are
+        constexpr_for<LPS>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          dma16_off<(i % 4) * 1024>(rsrc_c[i], wbase + (i / 4) * 4096, voff_c[i],
+                                    (uint32_t)(k0 * 2));
+        });
+      } else {
+        constexpr_for<LPS>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const uint32_t v =
+              (k0 + chunk_c[i] * 8) < a.K ? voff_c[i] + (uint32_t)(k0 * 2) : kOOB;
+          dma16_off<(i % 4) * 1024>(rsrc_c[i], wbase + (i / 4) * 4096, v, 0u);
+        });
+      }
+    } else if (kt < full_tiles) {
       issue_tile_loads<Cfg::kLoadsA, T>(rsrc_a, base, voff_a, kt * BK, wave);
       issue_tile_loads<Cfg::kLoadsB, T>(rsrc_b, base + Cfg::kABytes, voff_b, kt * BK, wave);
     } else {
@@ -124,12 +174,16 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   // its loads of that step have landed).
   auto fix_step = [&](int it) {
     if constexpr (kRagged) {
-      if (it < n_iter && kt_begin + it == a.k_tiles - 1) {
+      if (it < n_iter && korder.kt(it) == a.k_tiles - 1) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_u8* st = smem + (it % STAGES) * Cfg::kStageBytes;
-        fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, (kt_begin + it) * BK, a.K, tid);
-        fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, (kt_begin + it) * BK, a.K,
-                                         tid);
+        const int k0 = korder.kt(it) * BK;
+        if constexpr (CONTIG) {
+          fix_tail_chunks<LPS, 64>(st + wave * LPS * 1024, chunk_c, k0, a.K, lane);
+        } else {
+          fix_tail_chunks<Cfg::kLoadsA, T>(st, chunk_a, k0, a.K, tid);
+          fix_tail_chunks<Cfg::kLoadsB, T>(st + Cfg::kABytes, chunk_b, k0, a.K, tid);
+        }
       }
     }
   };

@@ -84,7 +84,7 @@ def test_config_names(lib):
 
     for w in WORKLOADS.values():
         chosen = lib.config_name(w.M, w.N, w.K)
-        m = re.match(r"^(.*)_k(\d+)_g(\d+)$", chosen)
+        m = re.match(r"^(.*)_k(\d+)_g(\d+)(_r\d+)?$", chosen)
         assert m and m.group(1) in names, chosen
         S = int(m.group(2))
         ws = lib.workspace_size(w.M, w.N, w.K)
@@ -92,6 +92,19 @@ def test_config_names(lib):
             assert ws == 0
         else:
             assert ws == S * w.M * ((w.N + 7) // 8 * 8) * 4, (w.name, chosen, ws)
+
+
+def test_degenerate_shapes_on_the_host(lib):
+    """Empty M, N or K: plan naming and workspace sizing must not fault on
+    the host (a zero tile count once divided by zero here)."""
+    for M, N, K in [(0, 16, 8), (4, 0, 8), (0, 0, 0), (5, 16, 0), (1, 1, 1)]:
+        assert lib.config_name(M, N, K)
+        assert lib.workspace_size(M, N, K) >= 0
+    so = lib._lib
+    fake = ctypes.c_void_p(0x10000)
+    # M == 0 or N == 0 returns before any device work
+    assert so.gemm_bf16(0, 16, 8, None, 8, None, 8, fake, 16, None) == lib.GEMM_OK
+    assert so.gemm_bf16(4, 0, 8, None, 8, None, 8, fake, 8, None) == lib.GEMM_OK
 
 
 def test_product_path_never_imports_the_oracle():
