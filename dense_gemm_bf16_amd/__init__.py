@@ -28,6 +28,16 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with dense_gemm_bf16_amd.build.build() "
         "(hipcc, gfx950).  There is no CPU fallback.")
 
+# PyTorch ships its own copy of the HIP runtime (same soname).  If this
+# library were loaded first, the process would end up with two HIP runtimes
+# (ours resolved from /opt/rocm, torch's from its own directory), and device
+# pointers and streams from one would be unknown to the other.  Loading torch
+# first makes the dynamic loader reuse its runtime for this library too.
+try:
+    import torch  # noqa: F401
+except ImportError:  # plain C-ABI use without torch: /opt/rocm's runtime
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _p = ctypes.c_int64, ctypes.c_void_p
 _lib.gemm_bf16.restype = ctypes.c_int

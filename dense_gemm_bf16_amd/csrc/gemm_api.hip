@@ -68,9 +68,10 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
 
 int64_t partial_ld(int64_t N) { return (N + 7) / 8 * 8; }
 
+
 size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
   if (p.splits <= 1) return 0;
-  return (size_t)p.splits * (size_t)M * (size_t)partial_ld(N) * sizeof(float);
+  return (size_t)p.splits * (size_t)M * (size_t)partial_ld(N) * 4;
 }
 
 // ------------------------------------------------------------ config choice
@@ -117,11 +118,10 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
     const int64_t per = (k_tiles + p->splits - 1) / p->splits;
     p->splits = (int)((k_tiles + per - 1) / per);
   }
-  if (p->k_rot > 0)
-    snprintf(p->name, sizeof p->name, "%s_k%d_g%d_r%d", p->tile->name, p->splits, p->group_m,
-             p->k_rot);
-  else
-    snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
+  const int n = snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
+  if (p->k_rot > 0 && n > 0 && n < (int)sizeof p->name)
+    snprintf(p->name + n, sizeof p->name - n, "_r%d", p->k_rot);
+
 }
 
 Plan choose_plan(int64_t M, int64_t N, int64_t K) {
@@ -166,6 +166,7 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
     } else if (u[1] == 'r' && sscanf(u + 2, "%d", &v) == 1 && v >= 0) {
       rot = v;
       *u = 0;
+
     } else {
       break;
     }
@@ -238,16 +239,16 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
     if (e != hipSuccess) return hip_fail(e);
     int rc = get_workspace(dev, stream, workspace_bytes(p, M, N), &ws);
     if (rc != GEMM_OK) return rc;
-    a.C = ws;
-    a.ldc = partial_ld(N);
-    a.c_split_stride = M * a.ldc;
+    a.part = (float*)ws;
+    a.ldp = partial_ld(N);
+    a.part_stride = M * a.ldp;
     flags |= kSplitK;
   }
   hipError_t e = t.launch(a, (int)grid, stream, flags);
   if (e != hipSuccess) return hip_fail(e);
   if (p.splits > 1) {
-    e = launch_splitk_reduce((const float*)ws, a.ldc, a.c_split_stride, p.splits, C, ldc,
-                             (int)M, (int)N, out_f32, stream);
+    e = launch_splitk_reduce(a.part, a.ldp, a.part_stride, p.splits, C, ldc, (int)M, (int)N,
+                             out_f32, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   return GEMM_OK;

@@ -78,7 +78,9 @@ struct KernelArgs {
   const uint16_t* B;
   void* C;                 // output, or the fp32 partial buffers when K is split
   int64_t lda, ldb, ldc;   // elements
-  int64_t c_split_stride;  // elements between the partial buffers of two slices
+  float* part;             // split K: fp32 partial buffer of slice 0 (M x ldp)
+  int64_t ldp;             // split K: row stride of the partial buffers (floats)
+  int64_t part_stride;     // split K: floats between the partial buffers of two slices
   int32_t M, N, K;
   int32_t tiles_m, tiles_n;
   int32_t k_tiles;            // ceil(K / BK)
@@ -94,11 +96,11 @@ struct KernelArgs {
 // K columns of the operands.  Rows of a power-of-two leading dimension would
 // otherwise send them all to the same few memory channels.  Each workgroup
 // still sums its steps in one fixed order, so results stay reproducible.
+// (Plain values captured by copy: held as a struct captured by reference in
+// the kernels' lambdas, the compiler once kept it in private memory and
+// read it there without the initialising store.)
 struct KOrder {
   int begin, n, rot;
-  __device__ KOrder(const KernelArgs& a, int t, int kt_begin, int n_iter)
-      : begin(kt_begin), n(n_iter),
-        rot(a.k_rot > 0 && n_iter > 0 ? (int)(((int64_t)t * a.k_rot) % n_iter) : 0) {}
   // global K-step of the workgroup's it-th step (0 <= it < n)
   __device__ __forceinline__ int kt(int it) const {
     const int j = it + rot;
@@ -106,10 +108,16 @@ struct KOrder {
   }
 };
 
+__device__ __forceinline__ KOrder make_korder(const KernelArgs& a, int t, int kt_begin,
+                                              int n_iter) {
+  const int rot = a.k_rot > 0 && n_iter > 0 ? (int)(((int64_t)t * a.k_rot) % n_iter) : 0;
+  return KOrder{kt_begin, n_iter, __builtin_amdgcn_readfirstlane(rot)};
+}
+
 // Variant flags of the kernel template.
 enum : int {
   kOutF32 = 1,   // store the fp32 sums (debug output) instead of bf16
-  kSplitK = 2,   // K is sliced across workgroups; write fp32 partials
+  kSplitK = 2,   // K is sliced across workgroups (fp32 partials, then a reduction)
   kRaggedK = 4,  // K % 8 != 0: patch the 16-byte chunk that straddles K
 };
 
@@ -165,13 +173,16 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t num_bytes)
 // One LDS-DMA load: 16 bytes per lane from rsrc.base + voff + soff into LDS
 // at lds_addr + 16*lane (M0 holds the wave's LDS base).  voff is range
 // checked (out of range reads zero); soff is not.  The s_nop covers the
-// M0-write -> LDS-DMA hazard.
+// M0-write -> LDS-DMA hazard.  lds_addr and soff are the same in every lane;
+// readfirstlane states that, so they are always given as scalar operands
+// (the compiler's divergence analysis cannot always prove it).
 __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds_addr, uint32_t voff,
                                       uint32_t soff) {
   asm volatile(
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(lds_addr),
-      "v"(voff), "s"(rsrc), "s"(soff)
+      "buffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(
+          __builtin_amdgcn_readfirstlane(lds_addr)),
+      "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
       : "memory");
 }
 
@@ -186,8 +197,9 @@ __device__ __forceinline__ void dma16_off(const u32x4& rsrc, uint32_t m0, uint32
   static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
   asm volatile(
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds" ::"{m0}"(m0),
-      "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF)
+      "buffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds" ::"{m0}"(
+          __builtin_amdgcn_readfirstlane(m0)),
+      "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "n"(OFF)
       : "memory");
 }
 
@@ -397,45 +409,65 @@ __device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::k
 
 // ---------------------------------------------------------------- epilogue
 
-template <typename Cfg, bool OUT_F32>
-__device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase,
-                                           const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                           int m_base, int n_base, int lane) {
+// Store one 32 x 32 accumulator block whose rows start at m0 and columns at
+// n0: lane l holds row m0 + l % 32, columns n0 + 8g + 4(l / 32) .. +3 in
+// elements 4g .. 4g+3 (g = 0..3).  Rows >= M and columns >= N are skipped.
+template <bool OUT_F32>
+__device__ __forceinline__ void store_block(void* Cbase, int64_t ld, const f32x16& blk, int m0,
+                                            int n0, int lane, int M, int N) {
+  const int m = m0 + (lane & 31);
+  if (m >= M) return;
 #pragma unroll
-  for (int fm = 0; fm < Cfg::kFragM; ++fm) {
-    const int m = m_base + fm * 32 + (lane & 31);
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int fn = 0; fn < Cfg::kFragN; ++fn) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // lane holds C[m][n .. n+3] in acc[fm][fn][4g .. 4g+3]
-        const int n = n_base + fn * 32 + 8 * g + 4 * (lane >> 5);
-        const f32x4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
-                         acc[fm][fn][4 * g + 3]};
-        if constexpr (OUT_F32) {
-          float* c = (float*)Cbase + (int64_t)m * a.ldc + n;
-          if (n + 3 < a.N) {
-            *(f32x4*)c = v;
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (n + j < a.N) c[j] = v[j];
-          }
-        } else {
-          const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
-          const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
-          __bf16* c = (__bf16*)Cbase + (int64_t)m * a.ldc + n;
-          if (n + 3 < a.N) {
-            *(bf16x4*)c = (bf16x4){lo[0], lo[1], hi[0], hi[1]};
-          } else {
-            const __bf16 e[4] = {lo[0], lo[1], hi[0], hi[1]};
-            for (int j = 0; j < 4; ++j)
-              if (n + j < a.N) c[j] = e[j];
-          }
-        }
+  for (int g = 0; g < 4; ++g) {
+    const int n = n0 + 8 * g + 4 * (lane >> 5);
+    const f32x4 v = {blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
+    if constexpr (OUT_F32) {
+      float* c = (float*)Cbase + (int64_t)m * ld + n;
+      if (n + 3 < N) {
+        *(f32x4*)c = v;
+      } else {
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) c[j] = v[j];
+      }
+    } else {
+      const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
+      const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
+      __bf16* c = (__bf16*)Cbase + (int64_t)m * ld + n;
+      if (n + 3 < N) {
+        *(bf16x4*)c = (bf16x4){lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        const __bf16 e[4] = {lo[0], lo[1], hi[0], hi[1]};
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) c[j] = e[j];
       }
     }
   }
+}
+
+// The wave's accumulator blocks into C (bf16, or fp32 for the debug output).
+template <typename Cfg, bool OUT_F32>
+__device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int64_t ld,
+                                           const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                           int m_base, int n_base, int lane) {
+#pragma unroll
+  for (int fm = 0; fm < Cfg::kFragM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < Cfg::kFragN; ++fn)
+      store_block<OUT_F32>(Cbase, ld, acc[fm][fn], m_base + fm * 32, n_base + fn * 32, lane,
+                           a.M, a.N);
+}
+
+// Epilogue of a K-slice: its unrounded fp32 sums go to its partial buffer;
+// the reduction kernel (gemm_reduce.hip) adds the slices in a fixed order.
+// (An in-kernel reduction by the last slice to finish a tile was measured
+// 2-3x slower: making the partials visible to the other XCDs needs a
+// release fence per workgroup, which writes back that XCD's L2.)
+template <typename Cfg>
+__device__ __forceinline__ void splitk_epilogue(const KernelArgs& a,
+                                                const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                int m_base, int n_base, int lane, int split) {
+  store_tile<Cfg, true>(a, a.part + (int64_t)split * a.part_stride, a.ldp, acc, m_base, n_base,
+                        lane);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -499,7 +531,7 @@ gemm_bf16_kernel(KernelArgs a) {
   const int kt_begin = split * a.k_tiles_per_split;
   const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
   const int n_iter = kt_end - kt_begin;
-  const KOrder korder(a, t, kt_begin, n_iter);
+  const KOrder korder = make_korder(a, t, kt_begin, n_iter);
   const int full_tiles = a.K / BK;  // K-steps that need no K check
 
   // ---- buffer resources: tile-origin based, range = valid rows ----------
@@ -716,11 +748,9 @@ gemm_bf16_kernel(KernelArgs a) {
   const int m_base = m0 + wm * Cfg::kWaveM;
   const int n_base = n0 + wn * Cfg::kWaveN;
   if constexpr (kSplit) {
-    // slice `split` owns partial buffer `split` (fp32, stride ldc)
-    store_tile<Cfg, true>(a, (float*)a.C + (int64_t)split * a.c_split_stride, acc, m_base,
-                          n_base, lane);
+    splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
   } else {
-    store_tile<Cfg, kF32>(a, a.C, acc, m_base, n_base, lane);
+    store_tile<Cfg, kF32>(a, a.C, a.ldc, acc, m_base, n_base, lane);
   }
 }
 

@@ -90,7 +90,7 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   const int kt_begin = split * a.k_tiles_per_split;
   const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
   const int n_iter = kt_end - kt_begin;
-  const KOrder korder(a, t, kt_begin, n_iter);
+  const KOrder korder = make_korder(a, t, kt_begin, n_iter);
   const int full_tiles = a.K / BK;
 
   const int rows_a = min(BM, a.M - m0);
@@ -228,10 +228,9 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   const int m_base = m0 + wm * Cfg::kWaveM;
   const int n_base = n0 + wn * Cfg::kWaveN;
   if constexpr (kSplit) {
-    store_tile<Cfg, true>(a, (float*)a.C + (int64_t)split * a.c_split_stride, acc, m_base,
-                          n_base, lane);
+    splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
   } else {
-    store_tile<Cfg, kF32>(a, a.C, acc, m_base, n_base, lane);
+    store_tile<Cfg, kF32>(a, a.C, a.ldc, acc, m_base, n_base, lane);
   }
 }
 

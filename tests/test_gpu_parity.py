@@ -108,8 +108,9 @@ def test_prefill_sampled(name):
 # ------------------------------------------------------------- edge cases
 
 def test_every_config_bit_exact_on_ragged_shape():
-    """Each built tile configuration, with and without split-K, on a shape
-    that is ragged in M, N and K: integer inputs, so bit-exact."""
+    """Each built tile configuration, with and without split-K and K-step
+    rotation, on a shape that is ragged in M, N and K: integer inputs, so
+    bit-exact."""
     import dense_gemm_bf16_amd as g
 
     M, N, K = 300, 520, 456
@@ -117,8 +118,9 @@ def test_every_config_bit_exact_on_ragged_shape():
     B = int_bf16(N, K, seed=102)
     ref16, ref64 = _oracle().gemm(A, B)
     for cfg in g.config_names():
-        for split in (1, 3):
-            name = f"{cfg}_k{split}"
+        # plain, split K, and split K with the K-step order rotated per tile
+        for suffix in ("_k1", "_k3", "_k2_g4_r1"):
+            name = cfg + suffix
             got = run_gemm(A, B, config=name)
             rep = check_bf16(got, ref16, None, K, exact=True)
             print(name, rep, flush=True)
