@@ -105,7 +105,10 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # Untimed warm-up: from an idle GPU the shader clock takes tens of ms to
+    # ramp up; 500 launches (~65 ms at 4096^3) reach the steady state that
+    # sustained runs of 1000+ launches also show.
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="square4096_normal")
     ap.add_argument("--config", default=None, help="force a kernel configuration")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,

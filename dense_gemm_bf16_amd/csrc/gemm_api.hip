@@ -81,14 +81,14 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 //    ring, K split so that about 256 workgroups stream B,
 //    K-step rotation on (the operands' power-of-two row strides otherwise
 //    send concurrent workgroups to the same memory channels: +10-28 %);
-//  * enough 256 x 256 tiles to fill the chip: the eight-wave ping-pong
-//    kernel for about one wave of tiles (4096^3), the register-staged
-//    256 x 256 x 64 kernel for several waves (M = 8192 prefill), no split;
+//  * enough 256 x 256 tiles to fill the chip (4096^3, M = 8192 prefill):
+//    the register-staged 256 x 256 x 64 kernel, no split (at steady clock
+//    1.5 % faster than the eight-wave ping-pong kernel at 4096^3 and 5 % at
+//    8192^3);
 //  * otherwise (M of a few hundred: the M = 256 decode layers, 512-row
 //    projections): register-staged 256 x 128 tiles, K split to about 256
 //    workgroups, rotation on.
 constexpr int kCUs = 256;
-constexpr const char* kPingPong = "t256x256x32_w2x4_s4_x2_p2";
 constexpr const char* kRegStageBig = "t256x256x64_w2x2_s2_x2_p6";
 constexpr const char* kRegStageMid = "t256x128x64_w2x2_s2_x2_p6";
 constexpr const char* kSkinny = "t32x128x64_w1x4_s6_x2_p0";
@@ -127,14 +127,14 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
 Plan choose_plan(int64_t M, int64_t N, int64_t K) {
   Plan p{};
   p.group_m = 4;
-  const TileConfig* big = find_tile_config(kPingPong);
+  const TileConfig* big = find_tile_config(kRegStageBig);
   const int64_t big_tiles = tiles_of(big, M, N);
   if (M <= 64) {
     p.tile = find_tile_config(kSkinny);
     p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
     p.k_rot = 1;
   } else if (big_tiles >= kCUs - kCUs / 8) {
-    p.tile = big_tiles >= 2 * kCUs ? find_tile_config(kRegStageBig) : big;
+    p.tile = big;
     p.splits = 1;
     p.k_rot = 0;
   } else {
