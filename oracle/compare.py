@@ -7,13 +7,15 @@ Criteria (the pages fix bf16 in/out with a wider accumulator but no
 tolerance; the readings below are stated in the design notes):
 
 * Integer-valued inputs: every partial sum is an integer below 2^24, exact in
-  fp32 in any order, so the bf16 result must equal the oracle's bit for bit
-  and the fp32 debug output must equal the fp64 sum exactly.
+  fp32 in any order, so the bf16 (or fp16) result must equal the oracle's bit
+  for bit and the fp32 debug output must equal the fp64 sum exactly.
 * Real-valued inputs: a correct fp32 accumulation may round differently from
   the exact sum, so an element passes if its bf16 value is within 1 ulp of
   the oracle's rounded result, or (near zero, where one bf16 ulp is finer
   than fp32 accumulation error) within an absolute floor of
-  1e-4 * sqrt(K) * sigma_A * sigma_B of the exact sum.
+  1e-4 * sqrt(K) * sigma_A * sigma_B of the exact sum.  The fp16 variant is
+  held to the same rule in fp16 ulps (both formats are sign-magnitude, so
+  adjacent values of either differ by one in the ordering key below).
 * fp32 debug output: |C32 - s| <= 1e-4 * sqrt(K) * sigma_A * sigma_B.
 """
 from __future__ import annotations
@@ -26,8 +28,17 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def f16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return b.view(np.float16).astype(np.float64)
+
+
+_DECODE = {"bf16": bf16_bits_to_f64, "f16": f16_bits_to_f64}
+
+
 def ulp_key(bits: np.ndarray) -> np.ndarray:
-    """Map bf16 patterns to integers ordered like the values they encode.
+    """Map bf16 (or fp16) patterns to integers ordered like the values they
+    encode.
 
     +0 and -0 both map to 0; adjacent bf16 values differ by 1."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
@@ -44,9 +55,9 @@ def abs_floor(K: int, sigma_a: float = 1.0, sigma_b: float = 1.0) -> float:
 
 
 def check_bf16(got_bits, ref_bits, ref_sum, K, sigma_a=1.0, sigma_b=1.0,
-               exact=False) -> dict:
-    """Compare GPU bf16 bits with the oracle.  Returns a report dict whose
-    ``ok`` field is the verdict."""
+               exact=False, fmt="bf16") -> dict:
+    """Compare GPU 16-bit results (bf16, or fp16 with ``fmt="f16"``) with the
+    oracle.  Returns a report dict whose ``ok`` field is the verdict."""
     got_bits = np.asarray(got_bits, np.uint16)
     ref_bits = np.asarray(ref_bits, np.uint16)
     d = ulp_dist(got_bits, ref_bits)
@@ -58,7 +69,7 @@ def check_bf16(got_bits, ref_bits, ref_sum, K, sigma_a=1.0, sigma_b=1.0,
         rep["n_fail"] = int((d != 0).sum())
         return rep
     floor = abs_floor(K, sigma_a, sigma_b)
-    err = np.abs(bf16_bits_to_f64(got_bits) - np.asarray(ref_sum, np.float64))
+    err = np.abs(_DECODE[fmt](got_bits) - np.asarray(ref_sum, np.float64))
     need_floor = d > 1
     fail = need_floor & ~(err <= floor)
     rep.update({"n_floor": int(need_floor.sum()), "n_fail": int(fail.sum()),

@@ -33,9 +33,14 @@
  *   - bf16 subnormal results are produced by clamping the quantum at 2^-133;
  *     overflow past the largest finite bf16 gives +-infinity.
  *
+ *   - The fp16-input variant (same page, measurement section: the
+ *     comparisons run on fp16 tensors) is the same sum over fp16 operands,
+ *     rounded once to fp16: IEEE binary16, round to nearest even,
+ *     subnormals down to 2^-24, overflow past 65504 to +-infinity.
+ *
  * Layouts (strides in elements):
  *   A(m,k) = A[m*lda + k], B(n,k) = B[n*ldb + k], C(m,n) = C[m*ldc + n].
- *   bf16 values are passed as their raw 16-bit patterns (uint16_t).
+ *   bf16 and fp16 values are passed as their raw 16-bit patterns (uint16_t).
  *
  * Parallelism: rows of C are split across OpenMP threads.  Each element is
  * still computed by one plain loop over k, so the result does not depend on
@@ -85,12 +90,104 @@ uint16_t oracle_round_f64_to_bf16(double x) {
   return (uint16_t)(u >> 16);
 }
 
+/* fp16 bit pattern -> double, from the IEEE 754 binary16 layout: sign bit,
+ * 5 exponent bits with bias 15, 10 fraction bits.  Exponent field 0 holds
+ * zero and the subnormals f * 2^-24; field 31 holds infinity and NaN;
+ * otherwise the value is (1024 + f) * 2^(e - 25).  Exact in double. */
+double oracle_f16_bits_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 31, f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+/* double -> fp16 bit pattern, round to nearest, ties to even, in one step.
+ *
+ * fp16 keeps 11 significant bits; normal numbers start at 2^-14 and the
+ * subnormal spacing is 2^-24.  As for bf16: with x = f * 2^e, 0.5 <= |f| < 1,
+ * the spacing around x is 2^(e-11), clamped below at 2^-24; round x / spacing
+ * to an integer (ties to even) and scale back.  The largest finite value is
+ * (2 - 2^-10) * 2^15 = 65504; a rounded result beyond it is infinite. */
+uint16_t oracle_round_f64_to_f16(double x) {
+  if (isnan(x)) return 0x7E00;
+  const uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isinf(x)) return sign | 0x7C00;
+  if (x == 0.0) return sign;
+  int e;
+  (void)frexp(x, &e);
+  int q = e - 11;
+  if (q < -24) q = -24;
+  const double r = fabs(ldexp(nearbyint(ldexp(x, -q)), q));
+  if (r > 65504.0) return sign | 0x7C00;
+  if (r == 0.0) return sign;
+  /* encode the exact fp16 value r */
+  int re;
+  const double rf = frexp(r, &re); /* r = rf * 2^re, 0.5 <= rf < 1 */
+  if (re - 1 < -14) /* subnormal: r = f * 2^-24 with f < 1024 */
+    return sign | (uint16_t)ldexp(r, 24);
+  const int field = re - 1 + 15;                      /* biased exponent */
+  const int frac = (int)ldexp(rf, 11) - 1024;         /* 10 stored bits */
+  return sign | (uint16_t)(field << 10) | (uint16_t)frac;
+}
+
+typedef double (*decode_fn)(uint16_t);
+typedef uint16_t (*round_fn)(double);
+
 /* One element: s = sum_k A(m,k) * B(n,k) in fp64, k ascending. */
-static double dot_f64(const uint16_t* a_row, const uint16_t* b_row, int64_t K) {
+static double dot_f64(decode_fn dec, const uint16_t* a_row, const uint16_t* b_row,
+                      int64_t K) {
   double s = 0.0;
   for (int64_t k = 0; k < K; ++k)
-    s += bf16_bits_to_f64(a_row[k]) * bf16_bits_to_f64(b_row[k]);
+    s += dec(a_row[k]) * dec(b_row[k]);
   return s;
+}
+
+static int gemm_any(decode_fn dec, round_fn rnd, int64_t M, int64_t N, int64_t K,
+                    const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    uint16_t* C, int64_t ldc, double* S, int64_t lds, int nthreads) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  if (lda < K || ldb < K) return -1;
+  if (C && ldc < N) return -1;
+  if (S && lds < N) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t n = 0; n < N; ++n) {
+      double s = dot_f64(dec, A + m * lda, B + n * ldb, K);
+      if (C) C[m * ldc + n] = rnd(s);
+      if (S) S[m * lds + n] = s;
+    }
+  }
+  (void)nthreads;
+  return 0;
+}
+
+static int entries_any(decode_fn dec, round_fn rnd, int64_t M, int64_t N, int64_t K,
+                       const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                       int64_t count, const int64_t* ms, const int64_t* ns,
+                       uint16_t* out16, double* out_f64, int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || count < 0) return -1;
+  if (lda < K || ldb < K) return -1;
+  for (int64_t i = 0; i < count; ++i)
+    if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+  for (int64_t i = 0; i < count; ++i) {
+    double s = dot_f64(dec, A + ms[i] * lda, B + ns[i] * ldb, K);
+    if (out16) out16[i] = rnd(s);
+    if (out_f64) out_f64[i] = s;
+  }
+  (void)nthreads;
+  return 0;
 }
 
 /* Full GEMM.  C (bf16, stride ldc) and S (fp64 sums, stride lds) are each
@@ -102,49 +199,42 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
                      uint16_t* C, int64_t ldc,
                      double* S, int64_t lds,
                      int nthreads) {
-  if (M < 0 || N < 0 || K < 0) return -1;
-  if (lda < K || ldb < K) return -1;
-  if (C && ldc < N) return -1;
-  if (S && lds < N) return -1;
-#ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
-#endif
-  for (int64_t m = 0; m < M; ++m) {
-    for (int64_t n = 0; n < N; ++n) {
-      double s = dot_f64(A + m * lda, B + n * ldb, K);
-      if (C) C[m * ldc + n] = oracle_round_f64_to_bf16(s);
-      if (S) S[m * lds + n] = s;
-    }
-  }
-  (void)nthreads;
-  return 0;
+  return gemm_any(bf16_bits_to_f64, oracle_round_f64_to_bf16, M, N, K, A, lda, B, ldb, C,
+                  ldc, S, lds, nthreads);
+}
+
+/* The same product over fp16 operands, C rounded to fp16. */
+int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
+                    const uint16_t* A, int64_t lda,
+                    const uint16_t* B, int64_t ldb,
+                    uint16_t* C, int64_t ldc,
+                    double* S, int64_t lds,
+                    int nthreads) {
+  return gemm_any(oracle_f16_bits_to_f64, oracle_round_f64_to_f16, M, N, K, A, lda, B, ldb,
+                  C, ldc, S, lds, nthreads);
 }
 
 /* Listed elements only: for i < count, element (ms[i], ns[i]) of the same
  * product.  Used where the full product is too large to evaluate on the
- * host in test time.  out_bf16 / out_f64 are each optional. */
+ * host in test time.  out16 / out_f64 are each optional. */
 int oracle_gemm_bf16_entries(int64_t M, int64_t N, int64_t K,
                              const uint16_t* A, int64_t lda,
                              const uint16_t* B, int64_t ldb,
                              int64_t count, const int64_t* ms, const int64_t* ns,
-                             uint16_t* out_bf16, double* out_f64,
+                             uint16_t* out16, double* out_f64,
                              int nthreads) {
-  if (M < 0 || N < 0 || K < 0 || count < 0) return -1;
-  if (lda < K || ldb < K) return -1;
-  for (int64_t i = 0; i < count; ++i)
-    if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
-#ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(static)
-#endif
-  for (int64_t i = 0; i < count; ++i) {
-    double s = dot_f64(A + ms[i] * lda, B + ns[i] * ldb, K);
-    if (out_bf16) out_bf16[i] = oracle_round_f64_to_bf16(s);
-    if (out_f64) out_f64[i] = s;
-  }
-  (void)nthreads;
-  return 0;
+  return entries_any(bf16_bits_to_f64, oracle_round_f64_to_bf16, M, N, K, A, lda, B, ldb,
+                     count, ms, ns, out16, out_f64, nthreads);
+}
+
+int oracle_gemm_f16_entries(int64_t M, int64_t N, int64_t K,
+                            const uint16_t* A, int64_t lda,
+                            const uint16_t* B, int64_t ldb,
+                            int64_t count, const int64_t* ms, const int64_t* ns,
+                            uint16_t* out16, double* out_f64,
+                            int nthreads) {
+  return entries_any(oracle_f16_bits_to_f64, oracle_round_f64_to_f16, M, N, K, A, lda, B,
+                     ldb, count, ms, ns, out16, out_f64, nthreads);
 }
 
 /* Threads OpenMP would use (for reporting the CPU baseline honestly). */
