@@ -135,19 +135,24 @@ uint16_t oracle_round_f64_to_f16(double x) {
   return sign | (uint16_t)(field << 10) | (uint16_t)frac;
 }
 
-typedef double (*decode_fn)(uint16_t);
 typedef uint16_t (*round_fn)(double);
 
-/* One element: s = sum_k A(m,k) * B(n,k) in fp64, k ascending. */
-static double dot_f64(decode_fn dec, const uint16_t* a_row, const uint16_t* b_row,
-                      int64_t K) {
+/* One element: s = sum_k A(m,k) * B(n,k) in fp64, k ascending; operands
+ * decoded as fp16 when half != 0, else as bf16.  (One loop per format, so
+ * the decode is inlined into it.) */
+static double dot_f64(int half, const uint16_t* a_row, const uint16_t* b_row, int64_t K) {
   double s = 0.0;
-  for (int64_t k = 0; k < K; ++k)
-    s += dec(a_row[k]) * dec(b_row[k]);
+  if (half) {
+    for (int64_t k = 0; k < K; ++k)
+      s += oracle_f16_bits_to_f64(a_row[k]) * oracle_f16_bits_to_f64(b_row[k]);
+  } else {
+    for (int64_t k = 0; k < K; ++k)
+      s += bf16_bits_to_f64(a_row[k]) * bf16_bits_to_f64(b_row[k]);
+  }
   return s;
 }
 
-static int gemm_any(decode_fn dec, round_fn rnd, int64_t M, int64_t N, int64_t K,
+static int gemm_any(int half, round_fn rnd, int64_t M, int64_t N, int64_t K,
                     const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                     uint16_t* C, int64_t ldc, double* S, int64_t lds, int nthreads) {
   if (M < 0 || N < 0 || K < 0) return -1;
@@ -160,7 +165,7 @@ static int gemm_any(decode_fn dec, round_fn rnd, int64_t M, int64_t N, int64_t K
 #endif
   for (int64_t m = 0; m < M; ++m) {
     for (int64_t n = 0; n < N; ++n) {
-      double s = dot_f64(dec, A + m * lda, B + n * ldb, K);
+      double s = dot_f64(half, A + m * lda, B + n * ldb, K);
       if (C) C[m * ldc + n] = rnd(s);
       if (S) S[m * lds + n] = s;
     }
@@ -169,7 +174,7 @@ static int gemm_any(decode_fn dec, round_fn rnd, int64_t M, int64_t N, int64_t K
   return 0;
 }
 
-static int entries_any(decode_fn dec, round_fn rnd, int64_t M, int64_t N, int64_t K,
+static int entries_any(int half, round_fn rnd, int64_t M, int64_t N, int64_t K,
                        const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                        int64_t count, const int64_t* ms, const int64_t* ns,
                        uint16_t* out16, double* out_f64, int nthreads) {
@@ -182,7 +187,7 @@ static int entries_any(decode_fn dec, round_fn rnd, int64_t M, int64_t N, int64_
 #pragma omp parallel for schedule(static)
 #endif
   for (int64_t i = 0; i < count; ++i) {
-    double s = dot_f64(dec, A + ms[i] * lda, B + ns[i] * ldb, K);
+    double s = dot_f64(half, A + ms[i] * lda, B + ns[i] * ldb, K);
     if (out16) out16[i] = rnd(s);
     if (out_f64) out_f64[i] = s;
   }
@@ -199,7 +204,7 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
                      uint16_t* C, int64_t ldc,
                      double* S, int64_t lds,
                      int nthreads) {
-  return gemm_any(bf16_bits_to_f64, oracle_round_f64_to_bf16, M, N, K, A, lda, B, ldb, C,
+  return gemm_any(0, oracle_round_f64_to_bf16, M, N, K, A, lda, B, ldb, C,
                   ldc, S, lds, nthreads);
 }
 
@@ -210,7 +215,7 @@ int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
                     uint16_t* C, int64_t ldc,
                     double* S, int64_t lds,
                     int nthreads) {
-  return gemm_any(oracle_f16_bits_to_f64, oracle_round_f64_to_f16, M, N, K, A, lda, B, ldb,
+  return gemm_any(1, oracle_round_f64_to_f16, M, N, K, A, lda, B, ldb,
                   C, ldc, S, lds, nthreads);
 }
 
@@ -223,7 +228,7 @@ int oracle_gemm_bf16_entries(int64_t M, int64_t N, int64_t K,
                              int64_t count, const int64_t* ms, const int64_t* ns,
                              uint16_t* out16, double* out_f64,
                              int nthreads) {
-  return entries_any(bf16_bits_to_f64, oracle_round_f64_to_bf16, M, N, K, A, lda, B, ldb,
+  return entries_any(0, oracle_round_f64_to_bf16, M, N, K, A, lda, B, ldb,
                      count, ms, ns, out16, out_f64, nthreads);
 }
 
@@ -233,7 +238,7 @@ int oracle_gemm_f16_entries(int64_t M, int64_t N, int64_t K,
                             int64_t count, const int64_t* ms, const int64_t* ns,
                             uint16_t* out16, double* out_f64,
                             int nthreads) {
-  return entries_any(oracle_f16_bits_to_f64, oracle_round_f64_to_f16, M, N, K, A, lda, B,
+  return entries_any(1, oracle_round_f64_to_f16, M, N, K, A, lda, B,
                      ldb, count, ms, ns, out16, out_f64, nthreads);
 }
 
