@@ -5,7 +5,8 @@ One step is one GEMM call on one batch of synthetic input that is already
 resident in HBM.  The default workload is the 4096^3 square GEMM with
 N(0,1) inputs; ``--workload`` selects any other shape of
 ``synthetic_inputs.WORKLOADS`` (prefill, decode, ragged) for measurements
-beyond the headline line.
+beyond the headline line, and ``--dtype f16`` measures the fp16-operand
+entry point on the same shapes.
 
 Printed: ONE JSON line with the contract fields, a ``roofline`` object for
 the GEMM kernel (achieved rate from HIP events on the launch stream against
@@ -33,7 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = ("bf16 GEMM TFLOP/s (and % MFMA peak / % HBM BW) at 4096³, "
           "prefill & decode shapes")
-PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_TFLOPS = 2500.0      # MI355X dense MFMA, bf16 and fp16 alike
 PEAK_GBPS = 8000.0        # MI355X HBM3E
 RIDGE = PEAK_TFLOPS * 1e12 / (PEAK_GBPS * 1e9)  # FLOP per byte
 CACHE_BYTES = 256 << 20   # Infinity Cache (MALL)
@@ -61,7 +62,8 @@ def kernel_source_hash() -> str:
 
 def measured_traffic(workload: str, config: str):
     """HBM bytes per launch from committed rocprofv3 PMC counters, only if
-    they were taken on the current kernel sources and the same config."""
+    they were taken on the current kernel sources and the same config.  The
+    key is the workload name, with "/f16" appended for fp16 operands."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -76,7 +78,7 @@ def measured_traffic(workload: str, config: str):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, A, B, target_s: float):
+def cpu_baseline(w, A, B, target_s: float, fmt: str = "bf16"):
     """The oracle (as it stands) on the first R rows of this workload: the
     whole workload if it fits the time target, else as many rows as do."""
     import oracle
@@ -84,11 +86,11 @@ def cpu_baseline(w, A, B, target_s: float):
     threads = oracle.max_threads()
     rows = min(w.M, 64)
     t0 = time.perf_counter()
-    oracle.gemm(A[:rows], B, K=w.K, want_f64=False)
+    oracle.gemm(A[:rows], B, K=w.K, want_f64=False, fmt=fmt)
     per_row = (time.perf_counter() - t0) / rows
     R = int(max(1, min(w.M, target_s / max(per_row, 1e-9))))
     t0 = time.perf_counter()
-    oracle.gemm(A[:R], B, K=w.K, want_f64=False)
+    oracle.gemm(A[:R], B, K=w.K, want_f64=False, fmt=fmt)
     dt = time.perf_counter() - t0
     what = "all" if R == w.M else f"first {R} of {w.M}"
     return {
@@ -111,6 +113,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="square4096_normal")
     ap.add_argument("--config", default=None, help="force a kernel configuration")
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
+                    help="operand type (f16: the gemm_f16 entry point)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target length of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,7 +155,8 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     M, N, K = w.M, w.N, w.K
-    A, B = w.make()
+    half = args.dtype == "f16"
+    A, B = w.make(fmt=args.dtype)
     flops = gemm_flops(M, N, K)
     nbytes = gemm_bytes(M, N, K)
     ai = flops / nbytes
@@ -169,8 +174,10 @@ def main() -> int:
         g.reserve_workspace(ws, stream)
     torch.cuda.synchronize()
 
+    entry = g.gemm_f16_ex if half else g.gemm_bf16_ex
+
     def step(i):
-        g.gemm_bf16_ex(args.config, M, N, K, dA, K, dBs[i % sets], K, dC, N, False, stream)
+        entry(args.config, M, N, K, dA, K, dBs[i % sets], K, dC, N, False, stream)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -198,12 +205,13 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS,
                 "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload, cfg)
+    roof["traffic"] = measured_traffic(args.workload + ("/f16" if half else ""), cfg)
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
 
+    metric = METRIC if not half else METRIC.replace("bf16 GEMM", "fp16-operand GEMM", 1)
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -213,7 +221,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K,
                    "kernel_config": cfg, "input_sets": sets,
@@ -223,8 +231,9 @@ def main() -> int:
         "roofline": roof,
     }
     if args.context:
-        a = dA.view(torch.bfloat16)
-        b = dBs[0].view(torch.bfloat16)
+        tdt = torch.float16 if half else torch.bfloat16
+        a = dA.view(tdt)
+        b = dBs[0].view(tdt)
         with torch.cuda.stream(stream):
             for _ in range(5):
                 torch.matmul(a, b.t())
@@ -237,7 +246,7 @@ def main() -> int:
         torch.cuda.synchronize()
         out["context"] = {"torch_matmul_tflops": round(flops / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12, 2)}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds, args.dtype)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -1,6 +1,7 @@
 """Python binding of ``libgemm_bf16.so``, the MI355X dense bf16 GEMM.
 
     C[M,N] = A[M,K] . B[N,K]^T     bf16 in, fp32 accumulate, bf16 out
+                                   (gemm_f16*: the same over fp16)
 
 The functions here only marshal arguments (sizes, device pointers, a HIP
 stream) to the C entry points of the same names declared in
@@ -61,6 +62,15 @@ _lib.gemm_bf16_workspace_size.restype = ctypes.c_size_t
 _lib.gemm_bf16_workspace_size.argtypes = [_i64, _i64, _i64]
 _lib.gemm_bf16_release_workspace.restype = ctypes.c_int
 _lib.gemm_bf16_release_workspace.argtypes = []
+_lib.gemm_f16.restype = ctypes.c_int
+_lib.gemm_f16.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.gemm_f16_f32out.restype = ctypes.c_int
+_lib.gemm_f16_f32out.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.gemm_f16_ex.restype = ctypes.c_int
+_lib.gemm_f16_ex.argtypes = [ctypes.c_char_p, _i64, _i64, _i64, _p, _i64, _p, _i64,
+                             _p, _i64, ctypes.c_int, _p]
+_lib.gemm_f16_config_at.restype = ctypes.c_char_p
+_lib.gemm_f16_config_at.argtypes = [ctypes.c_int]
 
 
 class GemmError(RuntimeError):
@@ -117,12 +127,34 @@ def gemm_bf16_ex(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32=False,
                              1 if out_f32 else 0, _stream(stream)))
 
 
-def gemm_bf16_status(M, N, K, A, lda, B, ldb, C, ldc, stream=0, out_f32=False,
-                     config=None) -> int:
-    """Raw status code of one call (for tests of argument checking)."""
+def gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """C = A . B^T over fp16 operands, fp16 output."""
+    _check(_lib.gemm_f16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                         _stream(stream)))
+
+
+def gemm_f16_f32out(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> None:
+    """fp16 operands, fp32 sums stored unrounded in C (float32)."""
+    _check(_lib.gemm_f16_f32out(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                _stream(stream)))
+
+
+def gemm_f16_ex(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32=False,
+                stream=None) -> None:
+    """As gemm_f16 with the kernel configuration named (None = automatic)."""
     cfg = None if config is None else config.encode()
-    return int(_lib.gemm_bf16_ex(cfg, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
-                                 1 if out_f32 else 0, stream))
+    _check(_lib.gemm_f16_ex(cfg, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                            1 if out_f32 else 0, _stream(stream)))
+
+
+def gemm_bf16_status(M, N, K, A, lda, B, ldb, C, ldc, stream=0, out_f32=False,
+                     config=None, half=False) -> int:
+    """Raw status code of one call (for tests of argument checking);
+    ``half`` calls gemm_f16_ex instead of gemm_bf16_ex."""
+    cfg = None if config is None else config.encode()
+    fn = _lib.gemm_f16_ex if half else _lib.gemm_bf16_ex
+    return int(fn(cfg, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                  1 if out_f32 else 0, stream))
 
 
 def config_name(M, N, K) -> str:
@@ -138,6 +170,19 @@ def config_at(i: int):
 def config_names() -> list[str]:
     out = []
     while (n := config_at(len(out))) is not None:
+        out.append(n)
+    return out
+
+
+def f16_config_at(i: int):
+    """The i-th configuration built for fp16 operands, or None past the end."""
+    n = _lib.gemm_f16_config_at(i)
+    return None if n is None else n.decode()
+
+
+def f16_config_names() -> list[str]:
+    out = []
+    while (n := f16_config_at(len(out))) is not None:
         out.append(n)
     return out
 
@@ -170,28 +215,39 @@ gemm_bf16_last_hip_error = last_hip_error
 gemm_bf16_reserve_workspace = reserve_workspace
 gemm_bf16_workspace_size = workspace_size
 gemm_bf16_release_workspace = release_workspace
+gemm_f16_config_at = f16_config_at
+
+
+def _row_stride(t, rows, cols):
+    """Leading dimension to pass for a 2-D tensor: its row stride, or for a
+    single row (whose stride is never used) the row length rounded up to 8."""
+    return t.stride(0) if rows > 1 else max(8, (cols + 7) // 8 * 8)
 
 
 def matmul(A, B, out=None, out_f32=False, config=None, stream=None):
     """Convenience form on torch tensors: A (M x K, rows contiguous), B (N x K,
-    rows contiguous), both bfloat16 on the GPU; returns C (M x N)."""
+    rows contiguous), both bfloat16 or both float16 on the GPU; returns C
+    (M x N) of the same type, or float32 with ``out_f32``."""
     import torch
 
-    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
-        raise TypeError("A and B must be torch.bfloat16")
+    if A.dtype != B.dtype or A.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("A and B must both be torch.bfloat16 or both torch.float16")
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
         raise ValueError("need A (M x K) and B (N x K)")
     if A.stride(1) != 1 or B.stride(1) != 1:
         raise ValueError("rows of A and B must be contiguous")
     M, K = A.shape
     N = B.shape[0]
+    out_dtype = torch.float32 if out_f32 else A.dtype
     if out is None:
-        out = torch.empty((M, N), device=A.device,
-                          dtype=torch.float32 if out_f32 else torch.bfloat16)
+        out = torch.empty((M, N), device=A.device, dtype=out_dtype)
+    if out.dtype != out_dtype or out.dim() != 2 or tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be a {M} x {N} {out_dtype} tensor")
     if out.stride(1) != 1:
         raise ValueError("rows of C must be contiguous")
-    lda = A.stride(0) if M > 1 else max(K, 8)
-    ldb = B.stride(0) if N > 1 else max(K, 8)
-    ldc = out.stride(0) if M > 1 else max(N, 8)
-    gemm_bf16_ex(config, M, N, K, A, lda, B, ldb, out, ldc, out_f32, stream)
+    lda = _row_stride(A, M, K)
+    ldb = _row_stride(B, N, K)
+    ldc = _row_stride(out, M, N)
+    fn = gemm_f16_ex if A.dtype == torch.float16 else gemm_bf16_ex
+    fn(config, M, N, K, A, lda, B, ldb, out, ldc, out_f32, stream)
     return out

@@ -1,5 +1,5 @@
-// C-ABI front end of the bf16 GEMM library: argument checks, the choice of
-// kernel configuration, split-K workspaces, launch.  The contract of every
+// C-ABI front end of the bf16 (and fp16) GEMM library: argument checks, the
+// choice of kernel configuration, split-K workspaces, launch.  The contract of every
 // entry point is stated in include/gemm_bf16.h.
 #include "../../include/gemm_bf16.h"
 
@@ -196,9 +196,11 @@ int check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
 }
 
 int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-        const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, hipStream_t stream) {
-  if (M == 0 || N == 0) return GEMM_OK;
+        const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
+        hipStream_t stream) {
   const TileConfig& t = *p.tile;
+  if (half && !t.f16) return GEMM_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return GEMM_OK;
   // 32-bit limits: tile-relative byte offsets of the operands, grid size,
   // and the int32 shape fields of the kernel.
   // (a tile's operand range plus the 4 KB a load may move its resource base
@@ -232,6 +234,7 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   a.k_rot = p.k_rot;
   int flags = out_f32 ? kOutF32 : 0;
   if ((K & 7) != 0) flags |= kRaggedK;
+  if (half) flags |= kF16;
   void* ws = nullptr;
   if (p.splits > 1) {
     int dev = 0;
@@ -247,15 +250,17 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   hipError_t e = t.launch(a, (int)grid, stream, flags);
   if (e != hipSuccess) return hip_fail(e);
   if (p.splits > 1) {
+    const int out_kind = out_f32 ? kStoreF32 : half ? kStoreF16 : kStoreBf16;
     e = launch_splitk_reduce(a.part, a.ldp, a.part_stride, p.splits, C, ldc, (int)M, (int)N,
-                             out_f32, stream);
+                             out_kind, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   return GEMM_OK;
 }
 
 int gemm_entry(const char* config, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-               const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, void* stream) {
+               const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
+               void* stream) {
   int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != GEMM_OK) return rc;
   Plan p{};
@@ -264,7 +269,17 @@ int gemm_entry(const char* config, int64_t M, int64_t N, int64_t K, const void* 
   } else {
     p = choose_plan(M, N, K);
   }
-  return run(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32, (hipStream_t)stream);
+  return run(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32, half, (hipStream_t)stream);
+}
+
+// The i-th table entry with f16 set (or with no condition), or NULL.
+const char* config_at(int i, bool f16_only) {
+  if (i < 0) return nullptr;
+  for (const TileConfig* t = tile_configs(); t->name; ++t) {
+    if (f16_only && !t->f16) continue;
+    if (i-- == 0) return t->name;
+  }
+  return nullptr;
 }
 
 thread_local char g_name_buf[64];
@@ -276,18 +291,35 @@ extern "C" {
 
 int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
               int64_t ldb, void* C, int64_t ldc, void* stream) {
-  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, false, stream);
+  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, false, false, stream);
 }
 
 int gemm_bf16_f32out(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, float* C, int64_t ldc, void* stream) {
-  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, true, stream);
+  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, true, false, stream);
 }
 
 int gemm_bf16_ex(const char* config, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                  const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* stream) {
-  return gemm::gemm_entry(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32 != 0, stream);
+  return gemm::gemm_entry(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32 != 0, false, stream);
 }
+
+int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, void* C, int64_t ldc, void* stream) {
+  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, false, true, stream);
+}
+
+int gemm_f16_f32out(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return gemm::gemm_entry(nullptr, M, N, K, A, lda, B, ldb, C, ldc, true, true, stream);
+}
+
+int gemm_f16_ex(const char* config, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                const void* B, int64_t ldb, void* C, int64_t ldc, int out_f32, void* stream) {
+  return gemm::gemm_entry(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32 != 0, true, stream);
+}
+
+const char* gemm_f16_config_at(int i) { return gemm::config_at(i, true); }
 
 const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return "invalid";
@@ -296,20 +328,16 @@ const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K) {
   return gemm::g_name_buf;
 }
 
-const char* gemm_bf16_config_at(int i) {
-  if (i < 0) return nullptr;
-  const gemm::TileConfig* t = gemm::tile_configs();
-  for (int j = 0; j < i; ++j)
-    if (!t[j].name) return nullptr;
-  return t[i].name;
-}
+const char* gemm_bf16_config_at(int i) { return gemm::config_at(i, false); }
 
 const char* gemm_bf16_status_string(int status) {
   switch (status) {
     case GEMM_OK: return "ok";
     case GEMM_ERR_INVALID_ARG: return "invalid argument (negative size, ld too small, or NULL)";
     case GEMM_ERR_MISALIGNED: return "misaligned (pointers need 16 B, leading dims a multiple of 8)";
-    case GEMM_ERR_UNSUPPORTED: return "unsupported (size beyond 32-bit offsets, or unknown config)";
+    case GEMM_ERR_UNSUPPORTED:
+      return "unsupported (size beyond 32-bit offsets, unknown config, or a config not built "
+             "for fp16)";
     case GEMM_ERR_HIP: return "HIP runtime error (see gemm_bf16_last_hip_error)";
     default: return "unknown status";
   }

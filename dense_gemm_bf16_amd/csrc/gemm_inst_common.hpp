@@ -6,9 +6,10 @@
 
 #include "gemm_launch.hpp"
 
-#define GEMM_DO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE) \
-  template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(const KernelArgs&, int, hipStream_t, int);
-#define GEMM_NO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE)
+#define GEMM_DO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16)   \
+  template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16>( \
+      const KernelArgs&, int, hipStream_t, int);
+#define GEMM_NO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16)
 
 #ifndef GEMM_INST_a
 #define GEMM_INST_a GEMM_NO_INST
@@ -67,13 +68,10 @@
 #ifndef GEMM_INST_s
 #define GEMM_INST_s GEMM_NO_INST
 #endif
-#ifndef GEMM_INST_t
-#define GEMM_INST_t GEMM_NO_INST
-#endif
 
 namespace gemm {
-#define GEMM_INSTANTIATE(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, TU) \
-  GEMM_INST_##TU(BM, BN, BK, WM, WN, ST, SWZ, PIPE)
+#define GEMM_INSTANTIATE(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU) \
+  GEMM_INST_##TU(BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16)
 GEMM_TILE_CONFIGS(GEMM_INSTANTIATE)
 #undef GEMM_INSTANTIATE
 }  // namespace gemm

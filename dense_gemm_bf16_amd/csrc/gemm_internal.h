@@ -11,13 +11,15 @@
 namespace gemm {
 
 // One compiled tile configuration.  `launch` takes the variant flags
-// (kOutF32 | kSplitK | kRaggedK) and enqueues the matching kernel.
+// (kOutF32 | kSplitK | kRaggedK | kF16) and enqueues the matching kernel;
+// kF16 only where `f16` is set.
 struct TileConfig {
   const char* name;  // e.g. "t256x256x64_w2x2_s2_x2"
   int bm, bn;        // output tile
   int bk;            // K elements per ring slot
   int threads;       // workgroup size
   int lds_bytes;     // static LDS per workgroup
+  bool f16;          // also built for fp16 operands
   hipError_t (*launch)(const KernelArgs&, int grid, hipStream_t, int flags);
 };
 
@@ -36,9 +38,10 @@ struct Plan {
 };
 
 // Fixed-order fp32 sum of S partial buffers P + s*slice_stride (rows of
-// stride ldp) into C, rounded to bf16 or stored as fp32.
+// stride ldp) into C, rounded to bf16 or fp16 or stored as fp32 (out_kind is
+// kStoreBf16, kStoreF16 or kStoreF32).
 hipError_t launch_splitk_reduce(const float* P, int64_t ldp, int64_t slice_stride, int S,
-                                void* C, int64_t ldc, int M, int N, bool out_f32,
+                                void* C, int64_t ldc, int M, int N, int out_kind,
                                 hipStream_t stream);
 
 }  // namespace gemm

@@ -67,6 +67,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -119,7 +122,16 @@ enum : int {
   kOutF32 = 1,   // store the fp32 sums (debug output) instead of bf16
   kSplitK = 2,   // K is sliced across workgroups (fp32 partials, then a reduction)
   kRaggedK = 4,  // K % 8 != 0: patch the 16-byte chunk that straddles K
+  kF16 = 8,      // operands (and the 16-bit output) are fp16 instead of bf16
 };
+
+// What the epilogue writes.
+enum : int { kStoreBf16 = 0, kStoreF16 = 1, kStoreF32 = 2 };
+
+template <int FLAGS>
+constexpr int store_kind() {
+  return (FLAGS & kOutF32) ? kStoreF32 : (FLAGS & kF16) ? kStoreF16 : kStoreBf16;
+}
 
 // ---------------------------------------------------------------- primitives
 
@@ -341,16 +353,28 @@ __device__ __forceinline__ void read_frags(const lds_u8* sa, const lds_u8* sb, i
   }
 }
 
-template <typename Cfg>
+// One 32 x 32 x 16 MFMA, D[n][m] += sum_k B[n][k] * A[m][k] (first operand
+// from B, second from A).  The fragments hold raw 16-bit patterns; HALF
+// reads them as fp16, otherwise as bf16.
+template <bool HALF>
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& b, const bf16x8& a,
+                                                const f32x16& c) {
+  if constexpr (HALF)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, b),
+                                                  __builtin_bit_cast(f16x8, a), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+}
+
+template <typename Cfg, bool HALF>
 __device__ __forceinline__ void mfma_block(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
                                            const bf16x8 (&fa)[Cfg::kFragM],
                                            const bf16x8 (&fb)[Cfg::kFragN]) {
-  // D[n][m] += sum_k B[n][k] * A[m][k]: first operand from B, second from A.
 #pragma unroll
   for (int fm = 0; fm < Cfg::kFragM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Cfg::kFragN; ++fn)
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+      acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
 }
 
 // Call f(std::integral_constant<int, i>) for i = 0 .. N-1 in order.
@@ -390,7 +414,7 @@ __device__ __forceinline__ void constexpr_for_window(int w, Fn&& f) {
 // The MFMAs of one substep with G loads spaced evenly between them: load q
 // goes after MFMA ceil((q+1)*n/G) - 1, and a scheduling barrier keeps each
 // load at its place in the MFMA stream.
-template <typename Cfg, int G, typename Dma>
+template <typename Cfg, bool HALF, int G, typename Dma>
 __device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                const bf16x8 (&fa)[Cfg::kFragM],
                                                const bf16x8 (&fb)[Cfg::kFragN], Dma&& dma) {
@@ -398,7 +422,7 @@ __device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::k
 #pragma unroll
   for (int j = 0; j < n; ++j) {
     const int fm = j / Cfg::kFragN, fn = j % Cfg::kFragN;
-    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+    acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
 #pragma unroll
     for (int q = (j * G) / n; q < ((j + 1) * G) / n; ++q) {
       dma(q);
@@ -412,7 +436,9 @@ __device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::k
 // Store one 32 x 32 accumulator block whose rows start at m0 and columns at
 // n0: lane l holds row m0 + l % 32, columns n0 + 8g + 4(l / 32) .. +3 in
 // elements 4g .. 4g+3 (g = 0..3).  Rows >= M and columns >= N are skipped.
-template <bool OUT_F32>
+// OUT (kStoreBf16 / kStoreF16 / kStoreF32) is the element type of C; the
+// 16-bit conversions round to nearest even.
+template <int OUT>
 __device__ __forceinline__ void store_block(void* Cbase, int64_t ld, const f32x16& blk, int m0,
                                             int n0, int lane, int M, int N) {
   const int m = m0 + (lane & 31);
@@ -421,13 +447,24 @@ __device__ __forceinline__ void store_block(void* Cbase, int64_t ld, const f32x1
   for (int g = 0; g < 4; ++g) {
     const int n = n0 + 8 * g + 4 * (lane >> 5);
     const f32x4 v = {blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
-    if constexpr (OUT_F32) {
+    if constexpr (OUT == kStoreF32) {
       float* c = (float*)Cbase + (int64_t)m * ld + n;
       if (n + 3 < N) {
         *(f32x4*)c = v;
       } else {
         for (int j = 0; j < 4; ++j)
           if (n + j < N) c[j] = v[j];
+      }
+    } else if constexpr (OUT == kStoreF16) {
+      const f16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, f16x2);
+      const f16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, f16x2);
+      _Float16* c = (_Float16*)Cbase + (int64_t)m * ld + n;
+      if (n + 3 < N) {
+        *(f16x4*)c = (f16x4){lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        const _Float16 e[4] = {lo[0], lo[1], hi[0], hi[1]};
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) c[j] = e[j];
       }
     } else {
       const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
@@ -444,8 +481,9 @@ __device__ __forceinline__ void store_block(void* Cbase, int64_t ld, const f32x1
   }
 }
 
-// The wave's accumulator blocks into C (bf16, or fp32 for the debug output).
-template <typename Cfg, bool OUT_F32>
+// The wave's accumulator blocks into C (bf16 or fp16, or fp32 for the debug
+// output).
+template <typename Cfg, int OUT>
 __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int64_t ld,
                                            const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
                                            int m_base, int n_base, int lane) {
@@ -453,7 +491,7 @@ __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int
   for (int fm = 0; fm < Cfg::kFragM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Cfg::kFragN; ++fn)
-      store_block<OUT_F32>(Cbase, ld, acc[fm][fn], m_base + fm * 32, n_base + fn * 32, lane,
+      store_block<OUT>(Cbase, ld, acc[fm][fn], m_base + fm * 32, n_base + fn * 32, lane,
                            a.M, a.N);
 }
 
@@ -466,8 +504,8 @@ template <typename Cfg>
 __device__ __forceinline__ void splitk_epilogue(const KernelArgs& a,
                                                 const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                 int m_base, int n_base, int lane, int split) {
-  store_tile<Cfg, true>(a, a.part + (int64_t)split * a.part_stride, a.ldp, acc, m_base, n_base,
-                        lane);
+  store_tile<Cfg, kStoreF32>(a, a.part + (int64_t)split * a.part_stride, a.ldp, acc, m_base,
+                             n_base, lane);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -500,7 +538,8 @@ gemm_bf16_kernel(KernelArgs a) {
   constexpr int LPS = Cfg::kLoadsPerStage;
   constexpr int LA = Cfg::kLoadsA;
   static_assert(PIPE != 2, "PIPE 2 is the ping-pong kernel");
-  constexpr bool kF32 = (FLAGS & kOutF32) != 0;
+  constexpr int kStore = store_kind<FLAGS>();
+  constexpr bool kHalf = (FLAGS & kF16) != 0;
   constexpr bool kSplit = (FLAGS & kSplitK) != 0;
   constexpr bool kRagged = (FLAGS & kRaggedK) != 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::kLdsBytes];
@@ -622,7 +661,7 @@ gemm_bf16_kernel(KernelArgs a) {
           const int cur = (b0 + kk) & 1, nxt = cur ^ 1;
           read_frags<Cfg, SWZ>(sa, sb, kk + 1, wm, wn, lane, fa[nxt], fb[nxt]);
           __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // DS reads
-          mfma_block<Cfg>(acc, fa[cur], fb[cur]);
+          mfma_block<Cfg, kHalf>(acc, fa[cur], fb[cur]);
           __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);  // MFMAs
         }
         const int cur = (b0 + Cfg::kSub - 1) & 1, nxt = cur ^ 1;
@@ -636,7 +675,7 @@ gemm_bf16_kernel(KernelArgs a) {
           read_frags<Cfg, SWZ>(na, na + Cfg::kABytes, 0, wm, wn, lane, fa[nxt], fb[nxt]);
           __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
         }
-        mfma_block<Cfg>(acc, fa[cur], fb[cur]);
+        mfma_block<Cfg, kHalf>(acc, fa[cur], fb[cur]);
         __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
       }
     }
@@ -728,7 +767,7 @@ gemm_bf16_kernel(KernelArgs a) {
           // window substep kk+1 of step it+STAGES-1
           constexpr_for_window<F, LPS>(kk + 1, [&](auto lo, auto hi) {
             constexpr int kLo = decltype(lo)::value, kHi = decltype(hi)::value;
-            mfma_block_dma<Cfg, kHi - kLo>(acc, fa[cur], fb[cur],
+            mfma_block_dma<Cfg, kHalf, kHi - kLo>(acc, fa[cur], fb[cur],
                                            [&](int q) { dma_one(it + STAGES - 1, kLo + q); });
           });
         }
@@ -740,7 +779,7 @@ gemm_bf16_kernel(KernelArgs a) {
         }
         // (no load of step it+STAGES exists in the last step, so nothing is
         // written into the slot that other waves may still be reading)
-        mfma_block_dma<Cfg, G0>(acc, fa[cur], fb[cur], [&](int q) { dma_one(it + STAGES, q); });
+        mfma_block_dma<Cfg, kHalf, G0>(acc, fa[cur], fb[cur], [&](int q) { dma_one(it + STAGES, q); });
       }
     }
   }
@@ -750,7 +789,7 @@ gemm_bf16_kernel(KernelArgs a) {
   if constexpr (kSplit) {
     splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
   } else {
-    store_tile<Cfg, kF32>(a, a.C, a.ldc, acc, m_base, n_base, lane);
+    store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
   }
 }
 

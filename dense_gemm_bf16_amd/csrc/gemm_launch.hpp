@@ -1,5 +1,5 @@
 // Launcher template for one tile configuration: maps the run-time variant
-// flags (kOutF32 | kSplitK | kRaggedK) to the instantiated kernels.  Each
+// flags (kOutF32 | kSplitK | kRaggedK | kF16) to the instantiated kernels.  Each
 // gemm_inst_*.hip file instantiates it for its configurations, so the
 // configurations compile in parallel.
 #pragma once
@@ -37,50 +37,67 @@ constexpr int lds_bytes_of() {
   return TileCfg<BM, BN, BK, WM, WN, PIPE == 6 ? 2 : ST, SWZ>::kLdsBytes;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE>
-hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
-  if (flags & kSplitK) flags &= ~kOutF32;  // split slices always write fp32 partials
+// The six (kOutF32, kSplitK, kRaggedK) combinations that occur, with the
+// operand-type bits E (0 or kF16).
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
+hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   switch (flags & 7) {
-    case 0: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 0>(a, grid, s);
-    case 1: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 1>(a, grid, s);
-    case 2: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 2>(a, grid, s);
-    case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 4>(a, grid, s);
-    case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 5>(a, grid, s);
-    default: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 6>(a, grid, s);
+    case 0: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 0>(a, grid, s);
+    case 1: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 1>(a, grid, s);
+    case 2: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 2>(a, grid, s);
+    case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
+    case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 5>(a, grid, s);
+    default: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 6>(a, grid, s);
   }
 }
 
-// Every built configuration:
-//   X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ, PIPE, TU)
-// where TU names the gemm_inst_<TU>.hip file that instantiates it.
-#define GEMM_TILE_CONFIGS(X)                                      \
-  X(t256x256x64_w2x2_s2_x2_p0, 256, 256, 64, 2, 2, 2, 2, 0, a)    \
-  X(t256x256x64_w2x2_s2_x2_p3, 256, 256, 64, 2, 2, 2, 2, 3, b)    \
-  X(t256x256x64_w2x2_s2_x2_p4, 256, 256, 64, 2, 2, 2, 2, 4, c)    \
-  X(t256x256x64_w2x2_s2_x2_p1, 256, 256, 64, 2, 2, 2, 2, 1, d)    \
-  X(t256x256x64_w2x4_s2_x2_p3, 256, 256, 64, 2, 4, 2, 2, 3, e)    \
-  X(t256x256x64_w2x4_s2_x2_p1, 256, 256, 64, 2, 4, 2, 2, 1, f)    \
-  X(t256x256x32_w2x4_s4_x2_p2, 256, 256, 32, 2, 4, 4, 2, 2, g)    \
-  X(t256x256x32_w2x4_s4_x2_p5, 256, 256, 32, 2, 4, 4, 2, 5, l)    \
-  X(t256x256x32_w2x2_s3_x2_p6, 256, 256, 32, 2, 2, 3, 2, 6, m)    \
-  X(t256x256x32_w2x2_s4_x2_p6, 256, 256, 32, 2, 2, 4, 2, 6, n)    \
-  X(t256x256x64_w2x2_s2_x2_p6, 256, 256, 64, 2, 2, 2, 2, 6, o)    \
-  X(t256x128x64_w2x2_s3_x2_p1, 256, 128, 64, 2, 2, 3, 2, 1, h)    \
-  X(t256x128x64_w2x2_s2_x2_p3, 256, 128, 64, 2, 2, 2, 2, 3, k)    \
-  X(t128x128x64_w2x2_s4_x2_p1, 128, 128, 64, 2, 2, 4, 2, 1, i)    \
-  X(t64x256x64_w1x4_s4_x2_p0, 64, 256, 64, 1, 4, 4, 2, 0, p)      \
-  X(t32x256x64_w1x4_s4_x2_p0, 32, 256, 64, 1, 4, 4, 2, 0, p)      \
-  X(t64x128x64_w1x4_s6_x2_p0, 64, 128, 64, 1, 4, 6, 2, 0, q)      \
-  X(t32x128x64_w1x4_s6_x2_p0, 32, 128, 64, 1, 4, 6, 2, 0, q)      \
-  X(t64x256x64_w1x4_s4_x2_p6, 64, 256, 64, 1, 4, 4, 2, 6, r)      \
-  X(t32x256x64_w1x4_s4_x2_p6, 32, 256, 64, 1, 4, 4, 2, 6, r)      \
-  X(t256x128x64_w2x2_s2_x2_p6, 256, 128, 64, 2, 2, 2, 2, 6, s)    \
-  X(t128x256x64_w2x2_s2_x2_p6, 128, 256, 64, 2, 2, 2, 2, 6, s)    \
-  X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, j)    \
-  X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, j)
+// F16: also instantiate the fp16-operand kernels.
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, bool F16>
+hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
+  if (flags & kSplitK) flags &= ~kOutF32;  // split slices always write fp32 partials
+  if (flags & kF16) {
+    if constexpr (F16)
+      return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, kF16>(a, grid, s, flags);
+    else
+      return hipErrorInvalidValue;
+  }
+  return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 0>(a, grid, s, flags);
+}
 
-#define GEMM_DECLARE_LAUNCH(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, TU) \
-  extern template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(const KernelArgs&, int, hipStream_t, int);
+// Every built configuration:
+//   X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ, PIPE, F16, TU)
+// where F16 = 1 also builds it for fp16 operands (the configurations the
+// shape rules pick, and one of each other kernel family), and TU names the
+// gemm_inst_<TU>.hip file that instantiates it.
+#define GEMM_TILE_CONFIGS(X)                                      \
+  X(t256x256x64_w2x2_s2_x2_p0, 256, 256, 64, 2, 2, 2, 2, 0, 0, a) \
+  X(t256x256x64_w2x2_s2_x2_p3, 256, 256, 64, 2, 2, 2, 2, 3, 0, b) \
+  X(t256x256x64_w2x2_s2_x2_p4, 256, 256, 64, 2, 2, 2, 2, 4, 0, c) \
+  X(t256x256x64_w2x2_s2_x2_p1, 256, 256, 64, 2, 2, 2, 2, 1, 1, d) \
+  X(t256x256x64_w2x4_s2_x2_p3, 256, 256, 64, 2, 4, 2, 2, 3, 0, e) \
+  X(t256x256x64_w2x4_s2_x2_p1, 256, 256, 64, 2, 4, 2, 2, 1, 0, f) \
+  X(t256x256x32_w2x4_s4_x2_p2, 256, 256, 32, 2, 4, 4, 2, 2, 0, g) \
+  X(t256x256x32_w2x4_s4_x2_p5, 256, 256, 32, 2, 4, 4, 2, 5, 1, l) \
+  X(t256x256x32_w2x2_s3_x2_p6, 256, 256, 32, 2, 2, 3, 2, 6, 0, m) \
+  X(t256x256x32_w2x2_s4_x2_p6, 256, 256, 32, 2, 2, 4, 2, 6, 0, n) \
+  X(t256x256x64_w2x2_s2_x2_p6, 256, 256, 64, 2, 2, 2, 2, 6, 1, o) \
+  X(t256x128x64_w2x2_s3_x2_p1, 256, 128, 64, 2, 2, 3, 2, 1, 0, h) \
+  X(t256x128x64_w2x2_s2_x2_p3, 256, 128, 64, 2, 2, 2, 2, 3, 0, k) \
+  X(t128x128x64_w2x2_s4_x2_p1, 128, 128, 64, 2, 2, 4, 2, 1, 0, i) \
+  X(t64x256x64_w1x4_s4_x2_p0, 64, 256, 64, 1, 4, 4, 2, 0, 0, p)   \
+  X(t32x256x64_w1x4_s4_x2_p0, 32, 256, 64, 1, 4, 4, 2, 0, 0, p)   \
+  X(t64x128x64_w1x4_s6_x2_p0, 64, 128, 64, 1, 4, 6, 2, 0, 1, q)   \
+  X(t32x128x64_w1x4_s6_x2_p0, 32, 128, 64, 1, 4, 6, 2, 0, 1, q)   \
+  X(t64x256x64_w1x4_s4_x2_p6, 64, 256, 64, 1, 4, 4, 2, 6, 0, r)   \
+  X(t32x256x64_w1x4_s4_x2_p6, 32, 256, 64, 1, 4, 4, 2, 6, 0, r)   \
+  X(t256x128x64_w2x2_s2_x2_p6, 256, 128, 64, 2, 2, 2, 2, 6, 1, s) \
+  X(t128x256x64_w2x2_s2_x2_p6, 128, 256, 64, 2, 2, 2, 2, 6, 1, s) \
+  X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, 0, j) \
+  X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, 0, j)
+
+#define GEMM_DECLARE_LAUNCH(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU) \
+  extern template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16>(  \
+      const KernelArgs&, int, hipStream_t, int);
 GEMM_TILE_CONFIGS(GEMM_DECLARE_LAUNCH)
 #undef GEMM_DECLARE_LAUNCH
 

@@ -57,7 +57,8 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   constexpr int LPS = Cfg::kLoadsPerStage;
   constexpr int LA = Cfg::kLoadsA;
   constexpr int SUB = Cfg::kSub;
-  constexpr bool kF32 = (FLAGS & kOutF32) != 0;
+  constexpr int kStore = store_kind<FLAGS>();
+  constexpr bool kHalf = (FLAGS & kF16) != 0;
   constexpr bool kSplit = (FLAGS & kSplitK) != 0;
   constexpr bool kRagged = (FLAGS & kRaggedK) != 0;
   static_assert(STAGES >= 3, "ping-pong refills a slot one step after it is read");
@@ -219,7 +220,7 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // ---- C(s): the MFMAs of step s -----------------------------------------
 #pragma unroll
-    for (int kk = 0; kk < SUB; ++kk) mfma_block<Cfg>(acc, fa[kk], fb[kk]);
+    for (int kk = 0; kk < SUB; ++kk) mfma_block<Cfg, kHalf>(acc, fa[kk], fb[kk]);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_barrier" ::: "memory");
   }
@@ -230,7 +231,7 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   if constexpr (kSplit) {
     splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
   } else {
-    store_tile<Cfg, kF32>(a, a.C, a.ldc, acc, m_base, n_base, lane);
+    store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
   }
 }
 

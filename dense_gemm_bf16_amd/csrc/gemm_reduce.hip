@@ -1,19 +1,19 @@
 // Split-K reduction:  C[m][n] = sum_{s=0}^{S-1} P_s[m][n], added in the fixed
-// order s = 0, 1, ..., S-1 in fp32, then rounded once to bf16 (round to
-// nearest even) or stored as fp32.  P_s are the unrounded partial products
+// order s = 0, 1, ..., S-1 in fp32, then rounded once to bf16 or fp16
+// (round to nearest even) or stored as fp32.  P_s are the unrounded partial products
 // of the K-slices written by the GEMM kernel; because the order never
 // changes, the result is bitwise reproducible and independent of which
 // slice finished first.
 //
 // Memory-bound and elementwise: each thread owns 8 consecutive columns of
-// one row (two 16-byte loads per slice, one 16-byte bf16 store), so every
+// one row (two 16-byte loads per slice, one 16-byte 16-bit store), so every
 // access is a coalesced 16-byte vector access.
 #include "gemm_internal.h"
 
 namespace gemm {
 namespace {
 
-template <bool OUT_F32>
+template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P,
                                                             int64_t ldp, int64_t slice_stride,
                                                             int S, void* __restrict__ C,
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       v[j] = acc;
     }
   }
-  if constexpr (OUT_F32) {
+  if constexpr (OUT == kStoreF32) {
     float* c = (float*)C + (int64_t)m * ldc + n;
     if (n + 8 <= N) {
       *(f32x4*)c = (f32x4){v[0], v[1], v[2], v[3]};
@@ -53,14 +53,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       for (int j = 0; j < 8 && n + j < N; ++j) c[j] = v[j];
     }
   } else {
-    __bf16* c = (__bf16*)C + (int64_t)m * ldc + n;
-    bf16x2 r[4];
+    // T: __bf16 or _Float16; the conversion rounds to nearest even
+    using T = std::conditional_t<OUT == kStoreF16, _Float16, __bf16>;
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    T* c = (T*)C + (int64_t)m * ldc + n;
+    t2 r[4];
     for (int j = 0; j < 4; ++j)
-      r[j] = __builtin_convertvector((f32x2){v[2 * j], v[2 * j + 1]}, bf16x2);
+      r[j] = __builtin_convertvector((f32x2){v[2 * j], v[2 * j + 1]}, t2);
     if (n + 8 <= N) {
-      typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-      *(bf16x8v*)c = (bf16x8v){r[0][0], r[0][1], r[1][0], r[1][1],
-                               r[2][0], r[2][1], r[3][0], r[3][1]};
+      *(t8*)c = (t8){r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
     } else {
       for (int j = 0; j < 8 && n + j < N; ++j) c[j] = r[j >> 1][j & 1];
     }
@@ -70,17 +72,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }  // namespace
 
 hipError_t launch_splitk_reduce(const float* P, int64_t ldp, int64_t slice_stride, int S,
-                                void* C, int64_t ldc, int M, int N, bool out_f32,
+                                void* C, int64_t ldc, int M, int N, int out_kind,
                                 hipStream_t stream) {
   const int64_t items = (int64_t)M * ((N + 7) / 8);
   const int64_t blocks = (items + 255) / 256;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  if (out_f32)
-    hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       P, ldp, slice_stride, S, C, ldc, M, N);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       P, ldp, slice_stride, S, C, ldc, M, N);
+  const dim3 grid((unsigned)blocks), block(256);
+  switch (out_kind) {
+    case kStoreF32:
+      hipLaunchKernelGGL(splitk_reduce_kernel<kStoreF32>, grid, block, 0, stream, P, ldp,
+                         slice_stride, S, C, ldc, M, N);
+      break;
+    case kStoreF16:
+      hipLaunchKernelGGL(splitk_reduce_kernel<kStoreF16>, grid, block, 0, stream, P, ldp,
+                         slice_stride, S, C, ldc, M, N);
+      break;
+    case kStoreBf16:
+      hipLaunchKernelGGL(splitk_reduce_kernel<kStoreBf16>, grid, block, 0, stream, P, ldp,
+                         slice_stride, S, C, ldc, M, N);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -61,20 +61,20 @@ __device__ __forceinline__ u32x4 mask_tail_chunk(u32x4 v, int k0, int K) {
 // The MFMAs of one substep with G operations spaced evenly between them
 // (op q right after MFMA j for q in [j*G/n, (j+1)*G/n), so several per MFMA
 // when G > n), each pinned in place by a scheduling barrier.
-template <typename Cfg, int G, int J = 0, typename Op>
+template <typename Cfg, bool HALF, int G, int J = 0, typename Op>
 __device__ __forceinline__ void mfma_interleave(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                 const bf16x8 (&fa)[Cfg::kFragM],
                                                 const bf16x8 (&fb)[Cfg::kFragN], Op&& op) {
   constexpr int n = Cfg::kFragM * Cfg::kFragN;
   if constexpr (J < n) {
     constexpr int fm = J / Cfg::kFragN, fn = J % Cfg::kFragN;
-    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+    acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
     constexpr int qlo = (J * G) / n, qhi = ((J + 1) * G) / n;
     constexpr_for<qhi - qlo>([&](auto qc) __attribute__((always_inline)) {
       op(std::integral_constant<int, qlo + decltype(qc)::value>{});
       __builtin_amdgcn_sched_barrier(0);
     });
-    mfma_interleave<Cfg, G, J + 1>(acc, fa, fb, op);
+    mfma_interleave<Cfg, HALF, G, J + 1>(acc, fa, fb, op);
   }
 }
 
@@ -98,7 +98,8 @@ gemm_bf16_regstage_kernel(KernelArgs a) {
   constexpr int SUB = Cfg::kSub;
   constexpr int LA = Cfg::kLoadsA;
   constexpr int L = Cfg::kLoadsPerStage;  // loads (and writes) per thread per step
-  constexpr bool kF32 = (FLAGS & kOutF32) != 0;
+  constexpr int kStore = store_kind<FLAGS>();
+  constexpr bool kHalf = (FLAGS & kF16) != 0;
   constexpr bool kSplit = (FLAGS & kSplitK) != 0;
   constexpr bool kRagged = (FLAGS & kRaggedK) != 0;
   static_assert(T == 256 || T == 512, "one or two waves per SIMD");
@@ -252,7 +253,7 @@ gemm_bf16_regstage_kernel(KernelArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         read_frags<Cfg, SWZ>(na, na + Cfg::kABytes, 0, wm, wn, lane, fa[nxt], fb[nxt]);
       }
-      mfma_interleave<Cfg, G>(acc, fa[cur], fb[cur], [&](auto qc) __attribute__((always_inline)) {
+      mfma_interleave<Cfg, kHalf, G>(acc, fa[cur], fb[cur], [&](auto qc) __attribute__((always_inline)) {
         constexpr int Q = decltype(qc)::value;
         // NBUF >= 3: loads, then writes; NBUF == 2: writes, then loads
         constexpr int NL = lhi - llo, NW = whi - wlo;
@@ -282,7 +283,7 @@ gemm_bf16_regstage_kernel(KernelArgs a) {
   if constexpr (kSplit) {
     splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
   } else {
-    store_tile<Cfg, kF32>(a, a.C, a.ldc, acc, m_base, n_base, lane);
+    store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
   }
 }
 

@@ -4,6 +4,8 @@
  *   C[M,N] = A[M,K] * B[N,K]^T      bf16 inputs, fp32 accumulation,
  *                                   bf16 output (or fp32 for the debug call)
  *
+ * (plus the same operation over fp16 operands: gemm_f16*, at the end)
+ *
  * The operation is the one defined on the page "Matrix Multiplication on
  * NVIDIA's Blackwell: A Four-Part Deep Dive" (section on the definition of
  * matrix multiplication: C is M x N inner products over K; naive-kernel
@@ -62,7 +64,8 @@ extern "C" {
 #define GEMM_ERR_INVALID_ARG 1 /* negative size, ld too small, NULL with work */
 #define GEMM_ERR_MISALIGNED 2  /* pointer not 16 B aligned or ld % 8 != 0 */
 #define GEMM_ERR_UNSUPPORTED 3 /* operand too large for 32-bit tile offsets,
-                                  unknown config name */
+                                  unknown config name, or a config not
+                                  built for fp16 passed to gemm_f16_ex */
 #define GEMM_ERR_HIP 4         /* a HIP runtime call failed; see
                                   gemm_bf16_last_hip_error */
 
@@ -97,14 +100,57 @@ int gemm_bf16_ex(const char* config,
                  void* C, int64_t ldc,
                  int out_f32, void* stream);
 
-/* Name of the configuration gemm_bf16 would choose for this shape, e.g.
- * "t256x256x32_w2x4_s4_x2_p2_k1_g4": tile BM x BN x BK, waves, ring stages,
- * LDS swizzle, load schedule, then K splits and GROUP_M.  Per-thread static
- * storage, valid until the thread's next call; never NULL. */
+/* Name of the configuration gemm_bf16 (and gemm_f16: the shape rules are the
+ * same for both operand types) would choose for this shape, e.g.
+ * "t256x256x64_w2x2_s2_x2_p6_k1_g4": tile BM x BN x BK, waves, ring stages,
+ * LDS swizzle, load schedule, then K splits and GROUP_M (and "_r<n>", the
+ * K-step rotation, when on).  Per-thread static storage, valid until the
+ * thread's next call; never NULL. */
 const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K);
 
 /* Enumerate the built configurations: the i-th name, or NULL past the end. */
 const char* gemm_bf16_config_at(int i);
+
+/* ------------------------------------------------------------------ fp16
+ * The same product over fp16 operands (IEEE binary16 bit patterns): fp16
+ * inputs, fp32 accumulation, fp16 output rounded to nearest even, with
+ * overflow past 65504 giving +-infinity.  This is the input type the page
+ * "Hand-writing a Blackwell GEMM: from 164 to 1400 TFLOP/s" measures with
+ * (section "how I measured": its checks run on fp16 tensors).  Layouts,
+ * shapes, alignment, ownership, workspaces, streams and status codes are
+ * exactly as for the bf16 calls above; the kernels are the same with the
+ * fp16 matrix-core instruction. */
+
+/* C = A * B^T with fp16 operands and fp16 output.  Returns a status code. */
+int gemm_f16(int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t lda,
+             const void* B, int64_t ldb,
+             void* C, int64_t ldc,
+             void* stream);
+
+/* Debug variant: fp16 operands, the fp32 sums stored unrounded (C is
+ * float*, ldc in floats, a multiple of 8).  Rounding it to fp16 gives
+ * gemm_f16's result. */
+int gemm_f16_f32out(int64_t M, int64_t N, int64_t K,
+                    const void* A, int64_t lda,
+                    const void* B, int64_t ldb,
+                    float* C, int64_t ldc,
+                    void* stream);
+
+/* gemm_f16 / gemm_f16_f32out with the configuration named explicitly.  Only
+ * the configurations gemm_f16_config_at enumerates are built for fp16; any
+ * other name returns GEMM_ERR_UNSUPPORTED.  config == NULL or "" selects
+ * automatically. */
+int gemm_f16_ex(const char* config,
+                int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda,
+                const void* B, int64_t ldb,
+                void* C, int64_t ldc,
+                int out_f32, void* stream);
+
+/* Enumerate the configurations built for fp16 operands: the i-th name, or
+ * NULL past the end. */
+const char* gemm_f16_config_at(int i);
 
 /* Human-readable text for a status code.  Static storage; never NULL. */
 const char* gemm_bf16_status_string(int status);

@@ -26,7 +26,8 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(gemm_bf16\w*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(gemm_(?:bf16|f16)\w*)\s*\(", text,
+                                 flags=re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -34,7 +35,8 @@ def test_header_declares_the_boundary():
     for n in ["gemm_bf16", "gemm_bf16_f32out", "gemm_bf16_ex", "gemm_bf16_config_name",
               "gemm_bf16_config_at", "gemm_bf16_status_string", "gemm_bf16_last_hip_error",
               "gemm_bf16_reserve_workspace", "gemm_bf16_workspace_size",
-              "gemm_bf16_release_workspace"]:
+              "gemm_bf16_release_workspace", "gemm_f16", "gemm_f16_f32out", "gemm_f16_ex",
+              "gemm_f16_config_at"]:
         assert n in names
 
 
@@ -72,6 +74,17 @@ def test_argument_checks_need_no_device(lib):
     assert so.gemm_bf16(8, 8, 12, fake, 12, fake, 16, fake, 8, None) == lib.GEMM_ERR_MISALIGNED
     assert so.gemm_bf16_ex(b"no_such_config", 8, 8, 8, fake, 8, fake, 8, fake, 8, 0,
                            None) == lib.GEMM_ERR_UNSUPPORTED
+    # the fp16 entry points share the checks
+    assert so.gemm_f16(-1, 8, 8, fake, 8, fake, 8, fake, 8, None) == lib.GEMM_ERR_INVALID_ARG
+    assert so.gemm_f16(8, 8, 8, odd, 8, fake, 8, fake, 8, None) == lib.GEMM_ERR_MISALIGNED
+    assert so.gemm_f16_f32out(8, 8, 12, fake, 12, fake, 16, fake, 8,
+                              None) == lib.GEMM_ERR_MISALIGNED
+    # a configuration not built for fp16 is refused before any device work
+    not_f16 = next(n for n in lib.config_names() if n not in lib.f16_config_names())
+    assert so.gemm_f16_ex(not_f16.encode(), 8, 8, 8, fake, 8, fake, 8, fake, 8, 0,
+                          None) == lib.GEMM_ERR_UNSUPPORTED
+    assert so.gemm_f16_ex(not_f16.encode(), 0, 8, 8, None, 8, None, 8, fake, 8, 0,
+                          None) == lib.GEMM_ERR_UNSUPPORTED
 
 
 def test_config_names(lib):
@@ -94,6 +107,21 @@ def test_config_names(lib):
             assert ws == S * w.M * ((w.N + 7) // 8 * 8) * 4, (w.name, chosen, ws)
 
 
+def test_f16_configs(lib):
+    """The fp16 configurations are a subset of the table that includes every
+    configuration the shape rules pick, so gemm_f16 serves every shape."""
+    f16 = lib.f16_config_names()
+    assert set(f16) <= set(lib.config_names()) and len(f16) == len(set(f16))
+    from synthetic_inputs import WORKLOADS
+
+    shapes = [(w.M, w.N, w.K) for w in WORKLOADS.values()]
+    shapes += [(1, 16, 8), (64, 64, 64), (65, 4096, 4096), (224, 8192, 1024), (8192, 256, 64)]
+    for M, N, K in shapes:
+        tile = re.match(r"^(.*)_k\d+_g\d+(_r\d+)?$", lib.config_name(M, N, K)).group(1)
+        assert tile in f16, (M, N, K, tile)
+    assert lib.f16_config_at(len(f16)) is None and lib.f16_config_at(-1) is None
+
+
 def test_degenerate_shapes_on_the_host(lib):
     """Empty M, N or K: plan naming and workspace sizing must not fault on
     the host (a zero tile count once divided by zero here)."""
@@ -105,6 +133,7 @@ def test_degenerate_shapes_on_the_host(lib):
     # M == 0 or N == 0 returns before any device work
     assert so.gemm_bf16(0, 16, 8, None, 8, None, 8, fake, 16, None) == lib.GEMM_OK
     assert so.gemm_bf16(4, 0, 8, None, 8, None, 8, fake, 8, None) == lib.GEMM_OK
+    assert so.gemm_f16(0, 16, 8, None, 8, None, 8, fake, 16, None) == lib.GEMM_OK
 
 
 def test_product_path_never_imports_the_oracle():
