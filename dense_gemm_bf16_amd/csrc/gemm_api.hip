@@ -82,14 +82,14 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 //    K-step rotation on (the operands' power-of-two row strides otherwise
 //    send concurrent workgroups to the same memory channels: +10-28 %);
 //  * enough 256 x 256 tiles to fill the chip (4096^3, M = 8192 prefill):
-//    the register-staged 256 x 256 x 64 kernel, no split (at steady clock
-//    1.5 % faster than the eight-wave ping-pong kernel at 4096^3 and 5 % at
-//    8192^3);
+//    the direct-to-LDS 256 x 256 x 64 kernel, no split (at steady clock 6 %
+//    faster than the register-staged kernel at 4096^3 and on both M = 8192
+//    prefill shapes);
 //  * otherwise (M of a few hundred: the M = 256 decode layers, 512-row
 //    projections): register-staged 256 x 128 tiles, K split to about 256
 //    workgroups, rotation on.
 constexpr int kCUs = 256;
-constexpr const char* kRegStageBig = "t256x256x64_w2x2_s2_x2_p6";
+constexpr const char* kBig = "t256x256x64_w2x2_s2_x2_p8";
 constexpr const char* kRegStageMid = "t256x128x64_w2x2_s2_x2_p6";
 constexpr const char* kSkinny = "t32x128x64_w1x4_s6_x2_p0";
 
@@ -127,7 +127,7 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
 Plan choose_plan(int64_t M, int64_t N, int64_t K) {
   Plan p{};
   p.group_m = 4;
-  const TileConfig* big = find_tile_config(kRegStageBig);
+  const TileConfig* big = find_tile_config(kBig);
   const int64_t big_tiles = tiles_of(big, M, N);
   if (M <= 64) {
     p.tile = find_tile_config(kSkinny);
@@ -235,6 +235,7 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   int flags = out_f32 ? kOutF32 : 0;
   if ((K & 7) != 0) flags |= kRaggedK;
   if (half) flags |= kF16;
+  if (K % t.bk != 0) flags |= kPartialK;
   void* ws = nullptr;
   if (p.splits > 1) {
     int dev = 0;

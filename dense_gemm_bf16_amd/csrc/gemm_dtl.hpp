@@ -1,0 +1,271 @@
+// Direct-to-LDS GEMM kernel: operand tiles go from global memory straight
+// into an S-slot LDS ring with LDS-DMA loads (`buffer_load_dwordx4 ... lds`,
+// no VGPR staging and no ds_write), each wave computes a 32-aligned block of
+// the tile from ds_read_b128 fragments with 32x32x16 MFMAs.
+//
+// Why this shape of kernel, from measurements on MI355X:
+//  * LDS writes through ds_write_b128 run at ~76-105 B/clk per CU, LDS reads
+//    at ~216-270 B/clk; staging every operand byte through VGPRs and
+//    ds_write (the register-staged kernel) keeps the LDS busy for a large
+//    share of each step.  LDS-DMA fills LDS from the texture path instead.
+//  * An LDS-DMA load with its addresses ready in registers costs its wave
+//    only a few cycles of issue (an MFMA stream with one such load per four
+//    32-cycle MFMAs stays ~95 % busy), so loads can sit between MFMAs.
+//  * The per-CU load path delivers ~64 B/clk; a 256 x 256 tile needs 32 B per
+//    MFMA-clock at full rate, so loads keep up.
+//
+// Per K-step X (SUB = BK/16 substeps), in every wave:
+//   substep kk < SUB-1:  MFMAs of kk with, between them, the ds_reads of
+//                        substep kk+1's fragments and load group kk+1 of
+//                        step X+S-1 (groups 1..F-1; F = 2 groups per step);
+//   substep SUB-1:       wait for step X+1's loads, barrier (this also frees
+//                        slot X % S: every wave has read its last fragments
+//                        of step X), then the MFMAs of substep SUB-1 with the
+//                        reads of step X+1's first fragments and group 0 of
+//                        step X+S (into the slot just freed) between them.
+// So a load is issued S-2 steps and a few substeps before the barrier that
+// needs it, and nothing waits on a load issued in the same step unless S = 2.
+//
+// The loads of a step: load i (A rows first, then B) of thread tid fills LDS
+// position s = i*T + tid of its operand's region: row s / CPR, chunk slot
+// tid % CPR, which holds logical 16-byte chunk (slot ^ swz(row)) of that row.
+// Each load keeps its own per-lane offset register (row*ld*2 + chunk*16, or
+// an out-of-range value for rows past M or N, which then read zero), so the
+// issue of a load is one M0 update and the instruction; the K offset of the
+// step goes in the (unchecked) scalar offset.  A step that reaches past K
+// (compiled only when K % BK != 0) moves the K offset into the range-checked
+// per-lane offset instead and sends chunks at or past K out of range; a
+// chunk that straddles K (K % 8 != 0) is trimmed in LDS once it has landed.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace gemm {
+
+template <int BM, int BN, int BK, int WM, int WN, int S, int SWZ, int FLAGS>
+__global__ __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
+                          amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void
+gemm_bf16_dtl_kernel(KernelArgs a) {
+  using Cfg = TileCfg<BM, BN, BK, WM, WN, S, SWZ>;
+  constexpr int T = Cfg::kThreads;
+  constexpr int CPR = Cfg::kCpr;
+  constexpr int SUB = Cfg::kSub;
+  constexpr int LA = Cfg::kLoadsA;
+  constexpr int L = Cfg::kLoadsPerStage;
+  constexpr int F = 2;  // load groups per step
+  constexpr int kStore = store_kind<FLAGS>();
+  constexpr bool kHalf = (FLAGS & kF16) != 0;
+  constexpr bool kSplit = (FLAGS & kSplitK) != 0;
+  constexpr bool kRagged = (FLAGS & kRaggedK) != 0;    // K % 8 != 0
+  constexpr bool kPartial = (FLAGS & kPartialK) != 0;  // K % BK != 0
+  static_assert(!kRagged || kPartial, "K % 8 != 0 implies K % BK != 0");
+  static_assert(SUB % 2 == 0, "fragment buffers alternate per substep, also across steps");
+  static_assert(F <= SUB, "a step's load groups fit in the substeps before its barrier");
+  static_assert(L % F == 0, "equal load groups");
+  static_assert((S - 2) * L + L / F < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::kLdsBytes];
+  lds_u8* const smem = (lds_u8*)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- which tile and which K-slice (as in the other kernels) -------------
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = kSplit ? logical / ntiles : 0;
+  const int t = logical - split * ntiles;
+  int tm, tn;
+  {
+    const int span = a.group_m * a.tiles_n;
+    const int gid = t / span;
+    const int first_m = gid * a.group_m;
+    const int gsz = min(a.tiles_m - first_m, a.group_m);
+    const int in = t - gid * span;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kt_begin = split * a.k_tiles_per_split;
+  const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
+  const int n_iter = kt_end - kt_begin;
+  const KOrder korder = make_korder(a, t, kt_begin, n_iter);
+  const int full_tiles = a.K / BK;  // K-steps wholly inside K
+
+  const int rows_a = min(BM, a.M - m0);
+  const int rows_b = min(BN, a.N - n0);
+  const u32x4 rsrc_a = make_rsrc(a.A + (int64_t)m0 * a.lda, (uint32_t)(rows_a * a.lda * 2));
+  const u32x4 rsrc_b = make_rsrc(a.B + (int64_t)n0 * a.ldb, (uint32_t)(rows_b * a.ldb * 2));
+
+  // Per-lane offsets of this thread's loads (see the header comment).
+  constexpr int RPI = T / CPR;  // rows covered by one load of all threads
+  static_assert(T % CPR == 0, "every load covers whole rows");
+  static_assert(swz_period_two<SWZ, CPR, RPI, (LA > L - LA ? LA : L - LA)>(),
+                "swz(i*RPI + r) depends on i only via i & 1");
+  const int r0 = tid / CPR, c0 = tid % CPR;
+  int chunk2[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) chunk2[p] = c0 ^ swz<SWZ, CPR>(p * RPI + r0);
+  uint32_t voff[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool is_a = i < LA;
+    const int ii = is_a ? i : i - LA;
+    const int row = ii * RPI + r0;
+    const int ld = (int)(is_a ? a.lda : a.ldb);
+    voff[i] = row < (is_a ? rows_a : rows_b) ? (uint32_t)(row * ld * 2 + chunk2[ii & 1] * 16)
+                                             : kOOB;
+  }
+
+  // LDS byte offset (within a slot) of load i's 1 KB of this wave.
+  auto lds_off = [&](int i) __attribute__((always_inline)) {
+    return (uint32_t)((i < LA ? 0 : Cfg::kABytes) + ((i < LA ? i : i - LA) * T + wave * 64) * 16);
+  };
+
+  // Load i of step Y (Y < n_iter).
+  auto dma_one = [&](int Y, int i) __attribute__((always_inline)) {
+    const int kt = korder.kt(Y);
+    const uint32_t dst = smem_addr + (uint32_t)((Y % S) * Cfg::kStageBytes) + lds_off(i);
+    const u32x4& rs = i < LA ? rsrc_a : rsrc_b;
+    if constexpr (kPartial) {
+      if (kt >= full_tiles) {
+        const int k0 = kt * BK;
+        const int c = chunk2[(i < LA ? i : i - LA) & 1];
+        const uint32_t v = (k0 + c * 8 < a.K) ? voff[i] + (uint32_t)(k0 * 2) : kOOB;
+        dma16(rs, dst, v, 0u);
+        return;
+      }
+    }
+    dma16(rs, dst, voff[i], (uint32_t)(kt * BK * 2));
+  };
+
+  // Trim the chunk that straddles K in this thread's part of step Y's slot
+  // (after its loads have landed).
+  auto trim_tail = [&](int Y) __attribute__((always_inline)) {
+    const int k0 = korder.kt(Y) * BK;
+    lds_u8* slot = smem + (Y % S) * Cfg::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int ii = i < LA ? i : i - LA;
+      const int keep = a.K - (k0 + chunk2[ii & 1] * 8);
+      if (keep > 0 && keep < 8) {
+        lds_u32x4* p = (lds_u32x4*)(slot + (i < LA ? 0 : Cfg::kABytes) + (ii * T + tid) * 16);
+        u32x4 v = *p;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int e = 2 * w;
+          v[w] &= (e + 1 < keep) ? 0xFFFFFFFFu : (e < keep ? 0x0000FFFFu : 0u);
+        }
+        *p = v;
+      }
+    }
+  };
+
+  // Wait until step Y's loads have landed in every wave and publish them;
+  // `later` steps after Y (whole) may still be in flight.
+  auto publish = [&](int Y, int later) __attribute__((always_inline)) {
+    if constexpr (kRagged) {
+      if (korder.kt(Y) == a.k_tiles - 1) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        trim_tail(Y);
+      }
+    }
+    ring_wait_barrier_n<L, S - 2>(later);
+  };
+
+  f32x16 acc[Cfg::kFragM][Cfg::kFragN];
+#pragma unroll
+  for (int i = 0; i < Cfg::kFragM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::kFragN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
+
+  // ---- prologue: steps 0..S-2 whole, group 0 of step S-1 -------------------
+  constexpr int G = L / F;
+#pragma unroll
+  for (int p = 0; p + 1 < S; ++p)
+    if (p < n_iter)
+#pragma unroll
+      for (int i = 0; i < L; ++i) dma_one(p, i);
+  const bool g0 = S - 1 < n_iter;
+  if (g0)
+#pragma unroll
+    for (int i = 0; i < G; ++i) dma_one(S - 1, i);
+  if (n_iter > 0) {
+    if constexpr (kRagged) {
+      if (korder.kt(0) == a.k_tiles - 1) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        trim_tail(0);
+      }
+    }
+    ring_wait_barrier_ng<L, S - 2, G>(min(S - 2, n_iter - 1), g0);
+    read_frags<Cfg, SWZ>(smem, smem + Cfg::kABytes, 0, wm, wn, lane, fa[0], fb[0]);
+  }
+
+  // ---- one K-step X.  V = 0: loads of steps X+S-1 (groups 1..F-1) and X+S
+  // (group 0); V = 1: only those of step X+S-1; V = 2: none.
+  auto step = [&](auto vc, int X) __attribute__((always_inline)) {
+    constexpr int V = decltype(vc)::value;
+    const lds_u8* sa = smem + (X % S) * Cfg::kStageBytes;
+    const lds_u8* sb = sa + Cfg::kABytes;
+    constexpr_for<SUB>([&](auto kc_) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kc_)::value;
+      constexpr int cur = kk & 1, nxt = cur ^ 1;
+      // load group carried by this substep, and the step it belongs to
+      constexpr bool kLast = kk == SUB - 1;
+      constexpr int grp = kLast ? 0 : kk + 1;
+      constexpr bool kLoads = kLast ? V == 0 : (V <= 1 && grp < F);
+      const int Y = kLast ? X + S : X + S - 1;
+      // fragments read during this substep: substep kk+1 of step X, or
+      // substep 0 of step X+1 once it is published
+      const lds_u8* ra = kLast ? smem + ((X + 1) % S) * Cfg::kStageBytes : sa;
+      constexpr int rkk = kLast ? 0 : kk + 1;
+      const bool reads = !kLast || V <= 1 || X + 1 < n_iter;
+      if constexpr (kLast) {
+        // in flight after step X+1: steps X+2 .. min(X+S-1, n_iter-1)
+        if (reads) publish(X + 1, V <= 1 ? S - 2 : min(S - 2, n_iter - 2 - X));
+      }
+      // The reads (in the order the next substep needs them) and the loads
+      // alternate between the MFMAs, evenly: issued back to back, the reads
+      // of four waves leaving a barrier together queue in the LDS ahead of
+      // their MFMAs, and a burst of loads fills the texture path.
+      constexpr int NR = Cfg::kFragM + Cfg::kFragN;
+      constexpr int NL = kLoads ? G : 0;
+      mfma_interleave<Cfg, kHalf, NR + NL>(
+          acc, fa[cur], fb[cur], [&](auto qc) __attribute__((always_inline)) {
+            constexpr int p = decltype(qc)::value;
+            constexpr int rb = p * NR / (NR + NL), rn = (p + 1) * NR / (NR + NL);
+            if constexpr (rn > rb) {
+              if (reads)
+                read_frag_one<Cfg, SWZ, frag_need_order<Cfg>(rb)>(ra, ra + Cfg::kABytes, rkk, wm,
+                                                                  wn, lane, fa[nxt], fb[nxt]);
+            } else {
+              dma_one(Y, grp * G + (p - rb));
+            }
+          });
+    });
+  };
+
+  int X = 0;
+  for (; X < n_iter - S; ++X) step(std::integral_constant<int, 0>{}, X);
+  if (n_iter >= S) {
+    step(std::integral_constant<int, 1>{}, X);
+    ++X;
+  }
+  for (; X < n_iter; ++X) step(std::integral_constant<int, 2>{}, X);
+
+  const int m_base = m0 + wm * Cfg::kWaveM;
+  const int n_base = n0 + wn * Cfg::kWaveN;
+  if constexpr (kSplit) {
+    splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
+  } else {
+    store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
+  }
+}
+
+}  // namespace gemm

@@ -68,6 +68,10 @@
 #ifndef GEMM_INST_s
 #define GEMM_INST_s GEMM_NO_INST
 #endif
+#ifndef GEMM_INST_t
+#define GEMM_INST_t GEMM_NO_INST
+#endif
+
 
 namespace gemm {
 #define GEMM_INSTANTIATE(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU) \

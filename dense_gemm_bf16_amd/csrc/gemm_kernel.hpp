@@ -73,6 +73,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr uint32_t kOOB = 0x80000000u;  // voffset that fails the range check
 
@@ -123,6 +124,7 @@ enum : int {
   kSplitK = 2,   // K is sliced across workgroups (fp32 partials, then a reduction)
   kRaggedK = 4,  // K % 8 != 0: patch the 16-byte chunk that straddles K
   kF16 = 8,      // operands (and the 16-bit output) are fp16 instead of bf16
+  kPartialK = 16,  // K % BK != 0 (only the direct-to-LDS kernel has a variant for it)
 };
 
 // What the epilogue writes.
@@ -366,6 +368,46 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& b, const bf16x8& a
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
 }
 
+// The order in which the MFMAs of a substep (fm-major, fn inner) first use
+// their fragments: entry r is the r-th fragment needed, numbered as in
+// read_frag_one (A fragments 0..kFragM-1, then B fragments).
+template <typename Cfg>
+constexpr int frag_need_order(int r) {
+  bool seen[Cfg::kFragM + Cfg::kFragN] = {};
+  int n = 0;
+  for (int j = 0; j < Cfg::kFragM * Cfg::kFragN; ++j) {
+    const int a = j / Cfg::kFragN, b = Cfg::kFragM + j % Cfg::kFragN;
+    if (!seen[b]) {
+      if (n++ == r) return b;
+      seen[b] = true;
+    }
+    if (!seen[a]) {
+      if (n++ == r) return a;
+      seen[a] = true;
+    }
+  }
+  return -1;
+}
+
+// Fragment IDX of read_frags alone (A fragments first, then B), so that the
+// reads of a substep can be spread between MFMAs.
+template <typename Cfg, int SWZ, int IDX>
+__device__ __forceinline__ void read_frag_one(const lds_u8* sa, const lds_u8* sb, int kk, int wm,
+                                              int wn, int lane, bf16x8 (&fa)[Cfg::kFragM],
+                                              bf16x8 (&fb)[Cfg::kFragN]) {
+  typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
+  constexpr int R = Cfg::kRowBytes, CPR = Cfg::kCpr;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  if constexpr (IDX < Cfg::kFragM) {
+    const int row = wm * Cfg::kWaveM + IDX * 32 + lrow;
+    fa[IDX] = *(lds_frag*)(sa + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
+  } else {
+    const int row = wn * Cfg::kWaveN + (IDX - Cfg::kFragM) * 32 + lrow;
+    fb[IDX - Cfg::kFragM] =
+        *(lds_frag*)(sb + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
+  }
+}
+
 template <typename Cfg, bool HALF>
 __device__ __forceinline__ void mfma_block(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
                                            const bf16x8 (&fa)[Cfg::kFragM],
@@ -429,6 +471,35 @@ __device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::k
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+}
+
+// The MFMAs of one substep with G operations spaced evenly between them
+// (op q right after MFMA j for q in [j*G/n, (j+1)*G/n), so several per MFMA
+// when G > n), each pinned in place by a scheduling barrier.
+template <typename Cfg, bool HALF, int G, int J = 0, typename Op>
+__device__ __forceinline__ void mfma_interleave(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                const bf16x8 (&fa)[Cfg::kFragM],
+                                                const bf16x8 (&fb)[Cfg::kFragN], Op&& op) {
+  constexpr int n = Cfg::kFragM * Cfg::kFragN;
+  if constexpr (J < n) {
+    constexpr int fm = J / Cfg::kFragN, fn = J % Cfg::kFragN;
+    acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
+    constexpr int qlo = (J * G) / n, qhi = ((J + 1) * G) / n;
+    constexpr_for<qhi - qlo>([&](auto qc) __attribute__((always_inline)) {
+      op(std::integral_constant<int, qlo + decltype(qc)::value>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    mfma_interleave<Cfg, HALF, G, J + 1>(acc, fa, fb, op);
+  }
+}
+
+// True if swz(i*RPI + r) == swz((i & 1)*RPI + r) for all i < n, r < RPI.
+template <int SWZ, int CPR, int RPI, int n>
+constexpr bool swz_period_two() {
+  for (int i = 0; i < n; ++i)
+    for (int r = 0; r < RPI; ++r)
+      if (swz<SWZ, CPR>(i * RPI + r) != swz<SWZ, CPR>((i & 1) * RPI + r)) return false;
+  return true;
 }
 
 // ---------------------------------------------------------------- epilogue

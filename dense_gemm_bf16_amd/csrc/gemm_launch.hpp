@@ -4,6 +4,7 @@
 // configurations compile in parallel.
 #pragma once
 
+#include "gemm_dtl.hpp"
 #include "gemm_kernel.hpp"
 #include "gemm_pingpong.hpp"
 #include "gemm_regstage.hpp"
@@ -14,7 +15,8 @@ namespace gemm {
 // PIPE 2 / 5: gemm_bf16_pingpong_kernel (8 waves as 2 x 4) with the
 // thread-strided / wave-contiguous dealing of loads;
 // PIPE 6: gemm_bf16_regstage_kernel (loads staged through ST register
-// buffers, two LDS slots).
+// buffers, two LDS slots);
+// PIPE 8: gemm_bf16_dtl_kernel (LDS-DMA straight into an ST-slot ring).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int FLAGS>
 hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
   if constexpr (PIPE == 2 || PIPE == 5) {
@@ -23,6 +25,9 @@ hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
                        dim3(grid), dim3(512), 0, s, a);
   } else if constexpr (PIPE == 6) {
     hipLaunchKernelGGL((gemm_bf16_regstage_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS>),
+                       dim3(grid), dim3(WM * WN * 64), 0, s, a);
+  } else if constexpr (PIPE == 8) {
+    hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS>),
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, ST, SWZ, PIPE, FLAGS>), dim3(grid),
@@ -37,18 +42,36 @@ constexpr int lds_bytes_of() {
   return TileCfg<BM, BN, BK, WM, WN, PIPE == 6 ? 2 : ST, SWZ>::kLdsBytes;
 }
 
-// The six (kOutF32, kSplitK, kRaggedK) combinations that occur, with the
-// operand-type bits E (0 or kF16).
+// The (kOutF32, kSplitK, kRaggedK) combinations that occur, with the fixed
+// bits E (kF16, kPartialK).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
 hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   switch (flags & 7) {
     case 0: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 0>(a, grid, s);
     case 1: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 1>(a, grid, s);
     case 2: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 2>(a, grid, s);
-    case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
-    case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 5>(a, grid, s);
-    default: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 6>(a, grid, s);
+    default: break;
   }
+  // K % 8 != 0 (the direct-to-LDS kernel handles it only in its K % BK != 0
+  // variant, which every such K selects)
+  if constexpr (PIPE != 8 || (E & kPartialK) != 0) {
+    switch (flags & 7) {
+      case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
+      case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 5>(a, grid, s);
+      default: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 6>(a, grid, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// Operand type E (0 or kF16) and, for the direct-to-LDS kernel, kPartialK.
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
+hipError_t launch_partial(const KernelArgs& a, int grid, hipStream_t s, int flags) {
+  if constexpr (PIPE == 8) {
+    if (flags & (kPartialK | kRaggedK))
+      return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | kPartialK>(a, grid, s, flags);
+  }
+  return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E>(a, grid, s, flags);
 }
 
 // F16: also instantiate the fp16-operand kernels.
@@ -57,11 +80,11 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   if (flags & kSplitK) flags &= ~kOutF32;  // split slices always write fp32 partials
   if (flags & kF16) {
     if constexpr (F16)
-      return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, kF16>(a, grid, s, flags);
+      return launch_partial<BM, BN, BK, WM, WN, ST, SWZ, PIPE, kF16>(a, grid, s, flags);
     else
       return hipErrorInvalidValue;
   }
-  return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 0>(a, grid, s, flags);
+  return launch_partial<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 0>(a, grid, s, flags);
 }
 
 // Every built configuration:
@@ -92,6 +115,7 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t32x256x64_w1x4_s4_x2_p6, 32, 256, 64, 1, 4, 4, 2, 6, 0, r)   \
   X(t256x128x64_w2x2_s2_x2_p6, 256, 128, 64, 2, 2, 2, 2, 6, 1, s) \
   X(t128x256x64_w2x2_s2_x2_p6, 128, 256, 64, 2, 2, 2, 2, 6, 1, s) \
+  X(t256x256x64_w2x2_s2_x2_p8, 256, 256, 64, 2, 2, 2, 2, 8, 1, t) \
   X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, 0, j) \
   X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, 0, j)
 

@@ -42,8 +42,6 @@
 
 namespace gemm {
 
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-
 // Zero the elements k >= K of one loaded 16-byte chunk holding k0 .. k0+7.
 __device__ __forceinline__ u32x4 mask_tail_chunk(u32x4 v, int k0, int K) {
   const int keep = K - k0;
@@ -56,35 +54,6 @@ __device__ __forceinline__ u32x4 mask_tail_chunk(u32x4 v, int k0, int K) {
     }
   }
   return v;
-}
-
-// The MFMAs of one substep with G operations spaced evenly between them
-// (op q right after MFMA j for q in [j*G/n, (j+1)*G/n), so several per MFMA
-// when G > n), each pinned in place by a scheduling barrier.
-template <typename Cfg, bool HALF, int G, int J = 0, typename Op>
-__device__ __forceinline__ void mfma_interleave(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                                const bf16x8 (&fa)[Cfg::kFragM],
-                                                const bf16x8 (&fb)[Cfg::kFragN], Op&& op) {
-  constexpr int n = Cfg::kFragM * Cfg::kFragN;
-  if constexpr (J < n) {
-    constexpr int fm = J / Cfg::kFragN, fn = J % Cfg::kFragN;
-    acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
-    constexpr int qlo = (J * G) / n, qhi = ((J + 1) * G) / n;
-    constexpr_for<qhi - qlo>([&](auto qc) __attribute__((always_inline)) {
-      op(std::integral_constant<int, qlo + decltype(qc)::value>{});
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    mfma_interleave<Cfg, HALF, G, J + 1>(acc, fa, fb, op);
-  }
-}
-
-// True if swz(i*RPI + r) == swz((i & 1)*RPI + r) for all i < n, r < RPI.
-template <int SWZ, int CPR, int RPI, int n>
-constexpr bool swz_period_two() {
-  for (int i = 0; i < n; ++i)
-    for (int r = 0; r < RPI; ++r)
-      if (swz<SWZ, CPR>(i * RPI + r) != swz<SWZ, CPR>((i & 1) * RPI + r)) return false;
-  return true;
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NBUF, int SWZ, int FLAGS>

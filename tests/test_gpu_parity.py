@@ -127,6 +127,28 @@ def test_every_config_bit_exact_on_ragged_shape():
             assert rep["ok"], (name, rep)
 
 
+def test_every_config_bit_exact_with_k_not_multiple_of_8():
+    """Each built configuration, plain and split with rotation, where a
+    16-byte chunk straddles K (K = 203) and the rows are padded with NaN:
+    the chunk's tail must be trimmed and nothing past K read."""
+    import dense_gemm_bf16_amd as g
+
+    M, N, K = 200, 136, 203
+    ld = 216
+    A = np.full((M, ld), 0x7FC0, np.uint16)
+    B = np.full((N, ld), 0x7FC0, np.uint16)
+    A[:, :K] = int_bf16(M, K, seed=103)
+    B[:, :K] = int_bf16(N, K, seed=104)
+    ref16, _ = _oracle().gemm(A, B, K=K)
+    for cfg in g.config_names():
+        for suffix in ("_k1", "_k2_g4_r1"):
+            name = cfg + suffix
+            got = run_gemm(A, B, K=K, config=name)
+            rep = check_bf16(got, ref16, None, K, exact=True)
+            print(name, rep, flush=True)
+            assert rep["ok"], (name, rep)
+
+
 @pytest.mark.parametrize("K", [1, 7, 8, 17, 63, 65, 200])
 def test_ragged_k(K):
     """K not a multiple of 8 (a 16-byte chunk straddles K) and not of 64;
