@@ -77,10 +77,12 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 // ------------------------------------------------------------ config choice
 // Static shape -> configuration rules, from sweeps on MI355X (HIP events,
 // cold B for the memory-bound shapes):
-//  * M <= 64 (small decode batches): 32 x 128 tiles with a six-slot LDS
-//    ring, K split so that about 256 workgroups stream B,
-//    K-step rotation on (the operands' power-of-two row strides otherwise
-//    send concurrent workgroups to the same memory channels: +10-28 %);
+//  * M <= 64 (small decode batches): the small-M kernel, one workgroup per
+//    BM x 32 block over all of K (BM = 32 up to M = 32, else 64), so
+//    N = 8192 gives 256 workgroups with no split-K pass; K-step rotation on
+//    (the operands' power-of-two row strides otherwise send concurrent
+//    workgroups to the same memory channels).  12-17 % faster than the
+//    earlier 32 x 128 tiles split four ways at M = 1 and 17, 3 % at M = 64;
 //  * enough 256 x 256 tiles to fill the chip (4096^3, M = 8192 prefill):
 //    the direct-to-LDS 256 x 256 x 64 kernel, no split (at steady clock 6 %
 //    faster than the register-staged kernel at 4096^3 and on both M = 8192
@@ -91,7 +93,8 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 constexpr int kCUs = 256;
 constexpr const char* kBig = "t256x256x64_w2x2_s2_x2_p8";
 constexpr const char* kRegStageMid = "t256x128x64_w2x2_s2_x2_p6";
-constexpr const char* kSkinny = "t32x128x64_w1x4_s6_x2_p0";
+constexpr const char* kSmallM32 = "t32x32x64_w1x1_s8_x2_p9";
+constexpr const char* kSmallM64 = "t64x32x64_w1x1_s6_x2_p9";
 
 int64_t tiles_of(const TileConfig* t, int64_t M, int64_t N) {
   return ((M + t->bm - 1) / t->bm) * ((N + t->bn - 1) / t->bn);
@@ -130,7 +133,7 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K) {
   const TileConfig* big = find_tile_config(kBig);
   const int64_t big_tiles = tiles_of(big, M, N);
   if (M <= 64) {
-    p.tile = find_tile_config(kSkinny);
+    p.tile = find_tile_config(M <= 32 ? kSmallM32 : kSmallM64);
     p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
     p.k_rot = 1;
   } else if (big_tiles >= kCUs - kCUs / 8) {

@@ -8,7 +8,8 @@ namespace gemm {
 
 const TileConfig* tile_configs() {
 #define GEMM_TABLE_ROW(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU)                 \
-  {#NAME, BM, BN, BK, WM * WN * 64, lds_bytes_of<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(), \
+  {#NAME, BM, BN, BK, PIPE == 9 ? 256 : WM * WN * 64,                                  \
+   lds_bytes_of<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(),                                     \
    F16 != 0, &launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16>},
   static const TileConfig table[] = {
       GEMM_TILE_CONFIGS(GEMM_TABLE_ROW){nullptr, 0, 0, 0, 0, 0, false, nullptr}};

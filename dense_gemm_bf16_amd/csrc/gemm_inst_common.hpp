@@ -71,6 +71,9 @@
 #ifndef GEMM_INST_t
 #define GEMM_INST_t GEMM_NO_INST
 #endif
+#ifndef GEMM_INST_u
+#define GEMM_INST_u GEMM_NO_INST
+#endif
 
 
 namespace gemm {

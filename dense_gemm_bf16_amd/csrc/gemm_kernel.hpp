@@ -504,52 +504,50 @@ constexpr bool swz_period_two() {
 
 // ---------------------------------------------------------------- epilogue
 
+// Store 4 consecutive fp32 sums v at row m, columns n .. n+3 of C, converted
+// to OUT (kStoreBf16 / kStoreF16 / kStoreF32; the 16-bit conversions round to
+// nearest even).  Columns >= N are skipped; the caller checks m < M.
+template <int OUT>
+__device__ __forceinline__ void store_quad(void* Cbase, int64_t ld, const f32x4& v, int m, int n,
+                                           int N) {
+  if constexpr (OUT == kStoreF32) {
+    float* c = (float*)Cbase + (int64_t)m * ld + n;
+    if (n + 3 < N) {
+      *(f32x4*)c = v;
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (n + j < N) c[j] = v[j];
+    }
+  } else {
+    // T: __bf16 or _Float16
+    using T = std::conditional_t<OUT == kStoreF16, _Float16, __bf16>;
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const t2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, t2);
+    const t2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, t2);
+    T* c = (T*)Cbase + (int64_t)m * ld + n;
+    if (n + 3 < N) {
+      *(t4*)c = (t4){lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      const T e[4] = {lo[0], lo[1], hi[0], hi[1]};
+      for (int j = 0; j < 4; ++j)
+        if (n + j < N) c[j] = e[j];
+    }
+  }
+}
+
 // Store one 32 x 32 accumulator block whose rows start at m0 and columns at
 // n0: lane l holds row m0 + l % 32, columns n0 + 8g + 4(l / 32) .. +3 in
 // elements 4g .. 4g+3 (g = 0..3).  Rows >= M and columns >= N are skipped.
-// OUT (kStoreBf16 / kStoreF16 / kStoreF32) is the element type of C; the
-// 16-bit conversions round to nearest even.
 template <int OUT>
 __device__ __forceinline__ void store_block(void* Cbase, int64_t ld, const f32x16& blk, int m0,
                                             int n0, int lane, int M, int N) {
   const int m = m0 + (lane & 31);
   if (m >= M) return;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int n = n0 + 8 * g + 4 * (lane >> 5);
-    const f32x4 v = {blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]};
-    if constexpr (OUT == kStoreF32) {
-      float* c = (float*)Cbase + (int64_t)m * ld + n;
-      if (n + 3 < N) {
-        *(f32x4*)c = v;
-      } else {
-        for (int j = 0; j < 4; ++j)
-          if (n + j < N) c[j] = v[j];
-      }
-    } else if constexpr (OUT == kStoreF16) {
-      const f16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, f16x2);
-      const f16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, f16x2);
-      _Float16* c = (_Float16*)Cbase + (int64_t)m * ld + n;
-      if (n + 3 < N) {
-        *(f16x4*)c = (f16x4){lo[0], lo[1], hi[0], hi[1]};
-      } else {
-        const _Float16 e[4] = {lo[0], lo[1], hi[0], hi[1]};
-        for (int j = 0; j < 4; ++j)
-          if (n + j < N) c[j] = e[j];
-      }
-    } else {
-      const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
-      const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
-      __bf16* c = (__bf16*)Cbase + (int64_t)m * ld + n;
-      if (n + 3 < N) {
-        *(bf16x4*)c = (bf16x4){lo[0], lo[1], hi[0], hi[1]};
-      } else {
-        const __bf16 e[4] = {lo[0], lo[1], hi[0], hi[1]};
-        for (int j = 0; j < 4; ++j)
-          if (n + j < N) c[j] = e[j];
-      }
-    }
-  }
+  for (int g = 0; g < 4; ++g)
+    store_quad<OUT>(Cbase, ld, (f32x4){blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]},
+                    m, n0 + 8 * g + 4 * (lane >> 5), N);
 }
 
 // The wave's accumulator blocks into C (bf16 or fp16, or fp32 for the debug

@@ -8,6 +8,7 @@
 #include "gemm_kernel.hpp"
 #include "gemm_pingpong.hpp"
 #include "gemm_regstage.hpp"
+#include "gemm_wavek.hpp"
 
 namespace gemm {
 
@@ -16,7 +17,9 @@ namespace gemm {
 // thread-strided / wave-contiguous dealing of loads;
 // PIPE 6: gemm_bf16_regstage_kernel (loads staged through ST register
 // buffers, two LDS slots);
-// PIPE 8: gemm_bf16_dtl_kernel (LDS-DMA straight into an ST-slot ring).
+// PIPE 8: gemm_bf16_dtl_kernel (LDS-DMA straight into an ST-slot ring);
+// PIPE 9: gemm_bf16_wavek_kernel (small M: four waves split each K-step of
+// one BM x 32 block; WM = WN = 1 name the block, 256 threads run it).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int FLAGS>
 hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
   if constexpr (PIPE == 2 || PIPE == 5) {
@@ -29,6 +32,10 @@ hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
   } else if constexpr (PIPE == 8) {
     hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS>),
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
+  } else if constexpr (PIPE == 9) {
+    static_assert(WM == 1 && WN == 1, "one block per workgroup");
+    hipLaunchKernelGGL((gemm_bf16_wavek_kernel<BM, BN, BK, ST, SWZ, FLAGS>), dim3(grid), dim3(256),
+                       0, s, a);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, ST, SWZ, PIPE, FLAGS>), dim3(grid),
                        dim3(WM * WN * 64), 0, s, a);
@@ -52,9 +59,9 @@ hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s, int flag
     case 2: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 2>(a, grid, s);
     default: break;
   }
-  // K % 8 != 0 (the direct-to-LDS kernel handles it only in its K % BK != 0
-  // variant, which every such K selects)
-  if constexpr (PIPE != 8 || (E & kPartialK) != 0) {
+  // K % 8 != 0 (the direct-to-LDS and small-M kernels handle it only in
+  // their K % BK != 0 variant, which every such K selects)
+  if constexpr ((PIPE != 8 && PIPE != 9) || (E & kPartialK) != 0) {
     switch (flags & 7) {
       case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
       case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 5>(a, grid, s);
@@ -64,10 +71,11 @@ hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s, int flag
   return hipErrorInvalidValue;
 }
 
-// Operand type E (0 or kF16) and, for the direct-to-LDS kernel, kPartialK.
+// Operand type E (0 or kF16) and, for the direct-to-LDS and small-M
+// kernels, kPartialK.
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
 hipError_t launch_partial(const KernelArgs& a, int grid, hipStream_t s, int flags) {
-  if constexpr (PIPE == 8) {
+  if constexpr (PIPE == 8 || PIPE == 9) {
     if (flags & (kPartialK | kRaggedK))
       return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | kPartialK>(a, grid, s, flags);
   }
@@ -116,6 +124,8 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t256x128x64_w2x2_s2_x2_p6, 256, 128, 64, 2, 2, 2, 2, 6, 1, s) \
   X(t128x256x64_w2x2_s2_x2_p6, 128, 256, 64, 2, 2, 2, 2, 6, 1, s) \
   X(t256x256x64_w2x2_s2_x2_p8, 256, 256, 64, 2, 2, 2, 2, 8, 1, t) \
+  X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 1, u)     \
+  X(t64x32x64_w1x1_s6_x2_p9, 64, 32, 64, 1, 1, 6, 2, 9, 1, u)     \
   X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, 0, j) \
   X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, 0, j)
 
