@@ -96,6 +96,16 @@ constexpr const char* kRegStageMid = "t256x128x64_w2x2_s2_x2_p6";
 constexpr const char* kSmallM32 = "t32x32x64_w1x1_s8_x2_p9";
 constexpr const char* kSmallM64 = "t64x32x64_w1x1_s6_x2_p9";
 
+// Shapes measured by the offline tuning sweep (dense_gemm_bf16_amd/tune.py):
+// exact (M, N, K) -> plan name, consulted before the rules below.
+struct TunedPlan {
+  int64_t M, N, K;
+  const char* plan;
+};
+constexpr TunedPlan kTuned[] = {
+#include "gemm_tuned.inc"
+    {0, 0, 0, nullptr}};
+
 int64_t tiles_of(const TileConfig* t, int64_t M, int64_t N) {
   return ((M + t->bm - 1) / t->bm) * ((N + t->bn - 1) / t->bn);
 }
@@ -127,7 +137,17 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
 
 }
 
-Plan choose_plan(int64_t M, int64_t N, int64_t K) {
+bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out);
+
+// The plan for a shape: the tuned table's entry if there is one (and its
+// tile is built for the operand type), else the rules.
+Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
+  for (const TunedPlan* e = kTuned; e->plan; ++e) {
+    if (e->M != M || e->N != N || e->K != K) continue;
+    Plan p{};
+    if (plan_from_name(e->plan, M, N, K, &p) && (!half || p.tile->f16)) return p;
+    break;
+  }
   Plan p{};
   p.group_m = 4;
   const TileConfig* big = find_tile_config(kBig);
@@ -271,7 +291,7 @@ int gemm_entry(const char* config, int64_t M, int64_t N, int64_t K, const void* 
   if (config && config[0]) {
     if (!plan_from_name(config, M, N, K, &p)) return GEMM_ERR_UNSUPPORTED;
   } else {
-    p = choose_plan(M, N, K);
+    p = choose_plan(M, N, K, half);
   }
   return run(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32, half, (hipStream_t)stream);
 }

@@ -1,0 +1,71 @@
+"""The offline tuning sweep's host side (no GPU): candidate plans are valid
+names the library accepts, the written table has the format the library
+compiles in, and every committed table entry is what the plan choice now
+returns for its shape."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TABLE = os.path.join(ROOT, "dense_gemm_bf16_amd", "csrc", "gemm_tuned.inc")
+PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d_x\d_p\d)_k(\d+)_g(\d+)(_r\d+)?$")
+ROW = re.compile(r'^\{(\d+), (\d+), (\d+), "([^"]+)"\},$')
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from dense_gemm_bf16_amd import build as b
+
+    if not os.path.exists(b.LIB):
+        b.build()
+    import dense_gemm_bf16_amd as g
+
+    return g
+
+
+def test_candidates_are_valid_plans(lib):
+    from dense_gemm_bf16_amd.tune import candidates, parse_tile
+
+    tiles = lib.config_names()
+    for M, N, K in [(4096, 4096, 4096), (256, 8192, 8192), (1, 8192, 8192),
+                    (8192, 28672, 8192), (300, 520, 456)]:
+        c = candidates(M, N, K, tiles)
+        assert c and len(c) == len(set(c))
+        for p in c:
+            m = PLAN.match(p)
+            assert m and m.group(1) in tiles, p
+            assert "_x0_" not in p and "_x1_" not in p
+            bm, bn, bk = parse_tile(m.group(1))
+            s = int(m.group(2))
+            n_tiles = -(-M // bm) * -(-N // bn)
+            if s > 1:
+                assert n_tiles < 256 and -(-K // bk) // s >= 4
+        # a shape whose 256 x 256 tiles fill the chip gets no split candidates
+        if (M, N, K) == (4096, 4096, 4096):
+            assert all(PLAN.match(p).group(2) == "1" for p in c)
+
+
+def test_written_table_format(tmp_path):
+    from dense_gemm_bf16_amd.tune import write_table
+
+    out = tmp_path / "t.inc"
+    write_table([(256, 8192, 8192, "t256x128x64_w2x2_s2_x2_p6_k4_g4_r1")], str(out), "note")
+    rows = [l for l in out.read_text().splitlines() if not l.startswith("//")]
+    assert rows == ['{256, 8192, 8192, "t256x128x64_w2x2_s2_x2_p6_k4_g4_r1"},']
+
+
+def test_committed_table_entries_are_used(lib):
+    rows = [l for l in open(TABLE).read().splitlines() if l and not l.startswith("//")]
+    for r in rows:
+        m = ROW.match(r)
+        assert m, r
+        M, N, K, plan = int(m.group(1)), int(m.group(2)), int(m.group(3)), m.group(4)
+        pm = PLAN.match(plan)
+        assert pm and pm.group(1) in lib.config_names(), plan
+        chosen = lib.config_name(M, N, K)
+        # the library normalises the split count (never more slices than
+        # K-steps); the tile, grouping and rotation are the table's
+        cm = PLAN.match(chosen)
+        assert cm.group(1) == pm.group(1) and cm.group(3) == pm.group(3), (plan, chosen)
+        assert (cm.group(4) or "") == (pm.group(4) or ""), (plan, chosen)
