@@ -82,7 +82,13 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 //    N = 8192 gives 256 workgroups with no split-K pass; K-step rotation on
 //    (the operands' power-of-two row strides otherwise send concurrent
 //    workgroups to the same memory channels).  12-17 % faster than the
-//    earlier 32 x 128 tiles split four ways at M = 1 and 17, 3 % at M = 64;
+//    earlier 32 x 128 tiles split four ways at M = 1 and 17, 6 % at M = 48.
+//    When the strips need more than one pass over the CUs (N = 10240: 320,
+//    N = 28672: 896), or M > 48 (a 64 x 32 strip reads twice as much A as
+//    B), the 32 x 128 / 64 x 128 tiles instead, K split to about 256
+//    workgroups: 33-34 vs 38-42 us at N = 10240 and M = 1, 32; 37 vs 57 us
+//    at 64 x 10240 x 8192, 80 vs 90 us at 32 x 28672 x 8192, 28 vs 33 us at
+//    64 x 4096 x 14336;
 //  * enough 256 x 256 tiles to fill the chip (4096^3, M = 8192 prefill):
 //    the direct-to-LDS 256 x 256 x 64 kernel, no split (at steady clock 6 %
 //    faster than the register-staged kernel at 4096^3 and on both M = 8192
@@ -95,6 +101,8 @@ constexpr const char* kBig = "t256x256x64_w2x2_s2_x2_p8";
 constexpr const char* kRegStageMid = "t256x128x64_w2x2_s2_x2_p6";
 constexpr const char* kSmallM32 = "t32x32x64_w1x1_s8_x2_p9";
 constexpr const char* kSmallM64 = "t64x32x64_w1x1_s6_x2_p9";
+constexpr const char* kSkinny32 = "t32x128x64_w1x4_s6_x2_p0";
+constexpr const char* kSkinny64 = "t64x128x64_w1x4_s6_x2_p0";
 
 // Shapes measured by the offline tuning sweep (dense_gemm_bf16_amd/tune.py):
 // exact (M, N, K) -> plan name, consulted before the rules below.
@@ -153,7 +161,13 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
   const TileConfig* big = find_tile_config(kBig);
   const int64_t big_tiles = tiles_of(big, M, N);
   if (M <= 64) {
-    p.tile = find_tile_config(M <= 32 ? kSmallM32 : kSmallM64);
+    // One BM x 32 strip per workgroup while the strips fit in one pass over
+    // the CUs (and BM x 32 strips re-read little A: M <= 48); otherwise
+    // 128-wide tiles, a quarter as many workgroups, split along K to fill.
+    const TileConfig* strip = find_tile_config(M <= 32 ? kSmallM32 : kSmallM64);
+    p.tile = (M <= 48 && tiles_of(strip, M, N) <= kCUs)
+                 ? strip
+                 : find_tile_config(M <= 32 ? kSkinny32 : kSkinny64);
     p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
     p.k_rot = 1;
   } else if (big_tiles >= kCUs - kCUs / 8) {

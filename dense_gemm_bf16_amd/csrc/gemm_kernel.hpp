@@ -274,7 +274,6 @@ struct TileCfg {
   static_assert(kBBytes % (kThreads * 16) == 0, "B tile splits into loads");
   static_assert(kLdsBytes <= 160 * 1024, "LDS is 160 KB per CU");
   static_assert(STAGES >= 2, "ring needs two slots");
-  static_assert(kLoadsPerStage * (STAGES - 1) < 64, "vmcnt range");
 };
 
 // ------------------------------------------------------------------- loads
