@@ -263,6 +263,16 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   const int n_base = n0 + wn * Cfg::kWaveN;
   if constexpr (kSplit) {
     splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
+  } else if constexpr (kStore != kStoreF32 && Cfg::kWaveN == 128 &&
+                       T / 64 * Cfg::kWaveM * 256 <= Cfg::kLdsBytes) {
+    // a tile wholly inside C goes out through LDS in whole row segments
+    if (m0 + BM <= a.M && n0 + BN <= a.N) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      store_tile_lds<Cfg, kStore>(smem + wave * (Cfg::kWaveM * 256), a.C, a.ldc, acc, m_base,
+                                  n_base, lane);
+    } else {
+      store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
+    }
   } else {
     store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
   }

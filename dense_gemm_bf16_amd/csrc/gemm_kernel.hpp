@@ -71,6 +71,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -503,6 +504,17 @@ constexpr bool swz_period_two() {
 
 // ---------------------------------------------------------------- epilogue
 
+// Four fp32 sums as four 16-bit values of OUT (kStoreBf16 / kStoreF16),
+// rounded to nearest even, packed little-endian into two dwords.
+template <int OUT>
+__device__ __forceinline__ u32x2 pack_quad(const f32x4& v) {
+  using T = std::conditional_t<OUT == kStoreF16, _Float16, __bf16>;
+  typedef T t2 __attribute__((ext_vector_type(2)));
+  const t2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, t2);
+  const t2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, t2);
+  return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Store 4 consecutive fp32 sums v at row m, columns n .. n+3 of C, converted
 // to OUT (kStoreBf16 / kStoreF16 / kStoreF32; the 16-bit conversions round to
 // nearest even).  Columns >= N are skipped; the caller checks m < M.
@@ -518,19 +530,13 @@ __device__ __forceinline__ void store_quad(void* Cbase, int64_t ld, const f32x4&
         if (n + j < N) c[j] = v[j];
     }
   } else {
-    // T: __bf16 or _Float16
-    using T = std::conditional_t<OUT == kStoreF16, _Float16, __bf16>;
-    typedef T t2 __attribute__((ext_vector_type(2)));
-    typedef T t4 __attribute__((ext_vector_type(4)));
-    const t2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, t2);
-    const t2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, t2);
-    T* c = (T*)Cbase + (int64_t)m * ld + n;
+    const u32x2 q = pack_quad<OUT>(v);
+    uint16_t* c = (uint16_t*)Cbase + (int64_t)m * ld + n;
     if (n + 3 < N) {
-      *(t4*)c = (t4){lo[0], lo[1], hi[0], hi[1]};
+      *(u32x2*)c = q;
     } else {
-      const T e[4] = {lo[0], lo[1], hi[0], hi[1]};
       for (int j = 0; j < 4; ++j)
-        if (n + j < N) c[j] = e[j];
+        if (n + j < N) c[j] = (uint16_t)(q[j >> 1] >> (16 * (j & 1)));
     }
   }
 }
@@ -561,6 +567,60 @@ __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int
     for (int fn = 0; fn < Cfg::kFragN; ++fn)
       store_block<OUT>(Cbase, ld, acc[fm][fn], m_base + fm * 32, n_base + fn * 32, lane,
                            a.M, a.N);
+}
+
+// The wave's whole kWaveM x 128 block of 16-bit C, staged through LDS so
+// that every global store writes whole row segments.  Stored straight from
+// the accumulators, a store instruction writes 16 bytes into each of 32 rows
+// (a lane holds 4 consecutive columns of one row), and the L2 takes one
+// partial-line write per row and instruction: on MI355X that made the
+// 256 x 256 tile's epilogue take 8-10 us.  Through LDS, 16 lanes write one
+// row's 256 bytes and an instruction covers 4 rows (8 whole 128-byte lines).
+//
+// `region` is this wave's kWaveM * 256 bytes of LDS, which no other wave
+// touches until the kernel ends; the caller has made sure the ring holds
+// nothing still needed (barrier after the last fragment reads) and that the
+// whole block lies inside C.  Layout: row r's 16-byte chunk c (columns
+// 8c .. 8c+7) sits at r*256 + 16 (c ^ (r % 16)), with its two 8-byte
+// halves swapped in rows with r % 32 >= 16; with the XOR, the 32 rows one
+// 8-byte write instruction touches and the 4 rows one 16-byte read touches
+// fall in distinct banks.
+template <typename Cfg, int OUT>
+__device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int64_t ld,
+                                               const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                               int m_base, int n_base, int lane) {
+  static_assert(OUT != kStoreF32, "16-bit output only");
+  static_assert(Cfg::kWaveN == 128, "rows of 16 chunks of 16 bytes");
+  constexpr int R = Cfg::kWaveN * 2;
+  // lane l's rows are fm*32 + l%32; column chunk fn*4 + g, half l/32
+  const int wr = lane & 31;
+  const uint32_t wsw = (uint32_t)(lane & 15);
+  const uint32_t whalf = (uint32_t)(((lane >> 5) ^ (lane >> 4)) & 1);
+#pragma unroll
+  for (int fm = 0; fm < Cfg::kFragM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < Cfg::kFragN; ++fn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t c = (uint32_t)(fn * 4 + g);
+        const uint32_t off = (uint32_t)((fm * 32 + wr) * R) + ((c ^ wsw) << 4) + (whalf << 3);
+        const f32x16& b = acc[fm][fn];
+        *(__attribute__((address_space(3))) u32x2*)(region + off) =
+            pack_quad<OUT>((f32x4){b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]});
+      }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // read back: instruction j covers rows 4j .. 4j+3, lane l row 4j + l/16,
+  // chunk l % 16
+  const int rr = lane >> 4, rc = lane & 15;
+  uint16_t* out = (uint16_t*)Cbase + (int64_t)(m_base + rr) * ld + n_base + rc * 8;
+#pragma unroll
+  for (int j = 0; j < Cfg::kWaveM / 4; ++j) {
+    const int r = 4 * j + rr;  // r % 16 = 4 (j % 4) + rr, r % 32 >= 16 iff j % 8 >= 4
+    const uint32_t off = (uint32_t)(r * R) + ((uint32_t)(rc ^ (4 * (j & 3) + rr)) << 4);
+    u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(region + off);
+    if ((j & 4) != 0) v = (u32x4){v[2], v[3], v[0], v[1]};
+    *(u32x4*)(out + (int64_t)(4 * j) * ld) = v;
+  }
 }
 
 // Epilogue of a K-slice: its unrounded fp32 sums go to its partial buffer;
