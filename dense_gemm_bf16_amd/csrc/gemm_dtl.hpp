@@ -259,23 +259,8 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   }
   for (; X < n_iter; ++X) step(std::integral_constant<int, 2>{}, X);
 
-  const int m_base = m0 + wm * Cfg::kWaveM;
-  const int n_base = n0 + wn * Cfg::kWaveN;
-  if constexpr (kSplit) {
-    splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
-  } else if constexpr (kStore != kStoreF32 && Cfg::kWaveN == 128 &&
-                       T / 64 * Cfg::kWaveM * 256 <= Cfg::kLdsBytes) {
-    // a tile wholly inside C goes out through LDS in whole row segments
-    if (m0 + BM <= a.M && n0 + BN <= a.N) {
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      store_tile_lds<Cfg, kStore>(smem + wave * (Cfg::kWaveM * 256), a.C, a.ldc, acc, m_base,
-                                  n_base, lane);
-    } else {
-      store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
-    }
-  } else {
-    store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
-  }
+  finish_tile<Cfg, kStore, kSplit>(a, smem, wave, m0, n0, acc, m0 + wm * Cfg::kWaveM,
+                                   n0 + wn * Cfg::kWaveN, lane, split);
 }
 
 }  // namespace gemm

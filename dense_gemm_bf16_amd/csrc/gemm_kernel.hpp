@@ -255,6 +255,8 @@ __host__ __device__ constexpr int swz(int row) {
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int SWZ>
 struct TileCfg {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
+  static constexpr int kBM = BM;
+  static constexpr int kBN = BN;
   static constexpr int kWaveM = BM / WAVES_M;
   static constexpr int kWaveN = BN / WAVES_N;
   static constexpr int kFragM = kWaveM / 32;
@@ -569,71 +571,115 @@ __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int
                            a.M, a.N);
 }
 
-// The wave's whole kWaveM x 128 block of 16-bit C, staged through LDS so
-// that every global store writes whole row segments.  Stored straight from
-// the accumulators, a store instruction writes 16 bytes into each of 32 rows
-// (a lane holds 4 consecutive columns of one row), and the L2 takes one
-// partial-line write per row and instruction: on MI355X that made the
-// 256 x 256 tile's epilogue take 8-10 us.  Through LDS, 16 lanes write one
-// row's 256 bytes and an instruction covers 4 rows (8 whole 128-byte lines).
+// ------------------------------------------------- epilogue through LDS
 //
-// `region` is this wave's kWaveM * 256 bytes of LDS, which no other wave
-// touches until the kernel ends; the caller has made sure the ring holds
-// nothing still needed (barrier after the last fragment reads) and that the
-// whole block lies inside C.  Layout: row r's 16-byte chunk c (columns
-// 8c .. 8c+7) sits at r*256 + 16 (c ^ (r % 16)), with its two 8-byte
-// halves swapped in rows with r % 32 >= 16; with the XOR, the 32 rows one
-// 8-byte write instruction touches and the 4 rows one 16-byte read touches
-// fall in distinct banks.
+// Stored straight from the accumulators, one store instruction writes 8 or
+// 16 bytes into each of 32 rows (a lane holds 4 consecutive columns of one
+// row), and the L2 takes one partial-line write per row and instruction: on
+// MI355X that made the 256 x 256 tile's bf16 epilogue take 8-10 us.  When
+// the LDS ring is idle (after the main loop) and the tile lies wholly
+// inside C, the waves instead write their accumulator blocks into LDS and
+// read them back by rows, so that 16 consecutive lanes store 256 contiguous
+// bytes of one row (whole 128-byte lines).
+//
+// Staging layout, per wave: row r of the wave block (kRB bytes) holds
+// 16-byte chunk c at r*kRB + 16 (c ^ sw(r)), sw(r) = r % 16, or (r / 2) % 8
+// for 128-byte rows; 16-bit output further swaps the two 8-byte halves of
+// every chunk in rows with r % 32 >= 16.  With that, the 32 rows one write
+// instruction touches, and the rows one 16-byte read touches, fall in
+// distinct banks.  Blocks too large for the ring go in passes of 32 rows
+// through two alternating buffers.
+template <typename Cfg, int OUT>
+struct LdsStage {
+  static constexpr int kE = OUT == kStoreF32 ? 4 : 2;  // bytes per element
+  static constexpr int kRB = Cfg::kWaveN * kE;         // bytes per staged row
+  static constexpr bool kShape =
+      kE == 4 ? (kRB == 256 || kRB == 512) : (kRB == 128 || kRB == 256);
+  static constexpr int kWaves = Cfg::kThreads / 64;
+  static constexpr bool kWhole = kWaves * Cfg::kWaveM * kRB <= Cfg::kLdsBytes;
+  static constexpr int kFmp = kWhole ? Cfg::kFragM : 1;  // 32-row blocks per pass
+  static constexpr int kBufs = kWhole ? 1 : 2;
+  static constexpr int kWaveBytes = kBufs * kFmp * 32 * kRB;
+  static constexpr bool kOk = kShape && kWaves * kWaveBytes <= Cfg::kLdsBytes;
+
+  __device__ static __forceinline__ uint32_t off(int r, int c) {
+    const int sw = kRB == 128 ? (r >> 1) & 7 : r & 15;
+    return (uint32_t)(r * kRB + ((c ^ sw) << 4));
+  }
+};
+
 template <typename Cfg, int OUT>
 __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int64_t ld,
                                                const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                int m_base, int n_base, int lane) {
-  static_assert(OUT != kStoreF32, "16-bit output only");
-  static_assert(Cfg::kWaveN == 128, "rows of 16 chunks of 16 bytes");
-  constexpr int R = Cfg::kWaveN * 2;
-  // lane l's rows are fm*32 + l%32; column chunk fn*4 + g, half l/32
-  const int wr = lane & 31;
-  const uint32_t wsw = (uint32_t)(lane & 15);
-  const uint32_t whalf = (uint32_t)(((lane >> 5) ^ (lane >> 4)) & 1);
+  using St = LdsStage<Cfg, OUT>;
+  static_assert(St::kOk, "staging fits the ring");
+  constexpr int kE = St::kE, kRB = St::kRB;
+  constexpr int LPR = kRB / 16;  // lanes per row when reading back
+  constexpr int RPI = 64 / LPR;  // rows per read instruction (divides 16)
+  static_assert(16 % RPI == 0, "a read instruction's rows share r / 16");
+  const int wr = lane & 31, hi = lane >> 5;
+  const int rr = lane / LPR, rc = lane % LPR;
+  uint8_t* out = (uint8_t*)Cbase + ((int64_t)(m_base + rr) * ld + n_base) * kE + rc * 16;
 #pragma unroll
-  for (int fm = 0; fm < Cfg::kFragM; ++fm)
+  for (int pass = 0; pass < Cfg::kFragM / St::kFmp; ++pass) {
+    lds_u8* buf = region + (pass % St::kBufs) * (St::kFmp * 32 * kRB);
 #pragma unroll
-    for (int fn = 0; fn < Cfg::kFragN; ++fn)
+    for (int fi = 0; fi < St::kFmp; ++fi) {
+      const int r = fi * 32 + wr;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t c = (uint32_t)(fn * 4 + g);
-        const uint32_t off = (uint32_t)((fm * 32 + wr) * R) + ((c ^ wsw) << 4) + (whalf << 3);
-        const f32x16& b = acc[fm][fn];
-        *(__attribute__((address_space(3))) u32x2*)(region + off) =
-            pack_quad<OUT>((f32x4){b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]});
-      }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  // read back: instruction j covers rows 4j .. 4j+3, lane l row 4j + l/16,
-  // chunk l % 16
-  const int rr = lane >> 4, rc = lane & 15;
-  uint16_t* out = (uint16_t*)Cbase + (int64_t)(m_base + rr) * ld + n_base + rc * 8;
+      for (int fn = 0; fn < Cfg::kFragN; ++fn)
 #pragma unroll
-  for (int j = 0; j < Cfg::kWaveM / 4; ++j) {
-    const int r = 4 * j + rr;  // r % 16 = 4 (j % 4) + rr, r % 32 >= 16 iff j % 8 >= 4
-    const uint32_t off = (uint32_t)(r * R) + ((uint32_t)(rc ^ (4 * (j & 3) + rr)) << 4);
-    u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(region + off);
-    if ((j & 4) != 0) v = (u32x4){v[2], v[3], v[0], v[1]};
-    *(u32x4*)(out + (int64_t)(4 * j) * ld) = v;
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& b = acc[pass * St::kFmp + fi][fn];
+          const f32x4 v = (f32x4){b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]};
+          if constexpr (kE == 4) {
+            *(__attribute__((address_space(3))) f32x4*)(buf + St::off(r, fn * 8 + 2 * g + hi)) = v;
+          } else {
+            const uint32_t h = (uint32_t)((hi ^ (wr >> 4)) & 1);
+            *(__attribute__((address_space(3))) u32x2*)(buf + St::off(r, fn * 4 + g) + (h << 3)) =
+                pack_quad<OUT>(v);
+          }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < St::kFmp * 32 / RPI; ++j) {
+      const int r = j * RPI + rr;
+      u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(buf + St::off(r, rc));
+      if constexpr (kE == 2)
+        if (((j * RPI) & 16) != 0) v = (u32x4){v[2], v[3], v[0], v[1]};
+      *(u32x4*)(out + (int64_t)((pass * St::kFmp * 32 + j * RPI) * kE) * ld) = v;
+    }
   }
 }
 
-// Epilogue of a K-slice: its unrounded fp32 sums go to its partial buffer;
-// the reduction kernel (gemm_reduce.hip) adds the slices in a fixed order.
+// The epilogue of every kernel: C (OUT), or with SPLIT the K-slice's
+// unrounded fp32 sums into its partial buffer (the reduction kernel in
+// gemm_reduce.hip adds the slices in a fixed order), through LDS for tiles
+// wholly inside C when the staging fits the ring, else straight from the
+// accumulators.  Called by all waves of the workgroup after the main loop
+// (the LDS path has a barrier); the ring must not be written again.
 // (An in-kernel reduction by the last slice to finish a tile was measured
 // 2-3x slower: making the partials visible to the other XCDs needs a
 // release fence per workgroup, which writes back that XCD's L2.)
-template <typename Cfg>
-__device__ __forceinline__ void splitk_epilogue(const KernelArgs& a,
-                                                const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                                int m_base, int n_base, int lane, int split) {
-  store_tile<Cfg, kStoreF32>(a, a.part + (int64_t)split * a.part_stride, a.ldp, acc, m_base,
-                             n_base, lane);
+template <typename Cfg, int OUT, bool SPLIT>
+__device__ __forceinline__ void finish_tile(const KernelArgs& a, lds_u8* smem, int wave, int m0,
+                                            int n0, const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                            int m_base, int n_base, int lane, int split) {
+  constexpr int kOut = SPLIT ? kStoreF32 : OUT;
+  void* const base = SPLIT ? (void*)(a.part + (int64_t)split * a.part_stride) : a.C;
+  const int64_t ld = SPLIT ? a.ldp : a.ldc;
+  if constexpr (LdsStage<Cfg, kOut>::kOk) {
+    if (m0 + Cfg::kBM <= a.M && n0 + Cfg::kBN <= a.N) {
+      // every wave is done with the ring: loads landed, fragments read
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      store_tile_lds<Cfg, kOut>(smem + wave * LdsStage<Cfg, kOut>::kWaveBytes, base, ld, acc,
+                                m_base, n_base, lane);
+      return;
+    }
+  }
+  store_tile<Cfg, kOut>(a, base, ld, acc, m_base, n_base, lane);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -912,13 +958,8 @@ gemm_bf16_kernel(KernelArgs a) {
     }
   }
 
-  const int m_base = m0 + wm * Cfg::kWaveM;
-  const int n_base = n0 + wn * Cfg::kWaveN;
-  if constexpr (kSplit) {
-    splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
-  } else {
-    store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
-  }
+  finish_tile<Cfg, kStore, kSplit>(a, smem, wave, m0, n0, acc, m0 + wm * Cfg::kWaveM,
+                                   n0 + wn * Cfg::kWaveN, lane, split);
 }
 
 }  // namespace gemm

@@ -226,13 +226,8 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   }
   if (grp == 0) asm volatile("s_barrier" ::: "memory");  // group 0 idles in the last phase
 
-  const int m_base = m0 + wm * Cfg::kWaveM;
-  const int n_base = n0 + wn * Cfg::kWaveN;
-  if constexpr (kSplit) {
-    splitk_epilogue<Cfg>(a, acc, m_base, n_base, lane, split);
-  } else {
-    store_tile<Cfg, kStore>(a, a.C, a.ldc, acc, m_base, n_base, lane);
-  }
+  finish_tile<Cfg, kStore, kSplit>(a, smem, wave, m0, n0, acc, m0 + wm * Cfg::kWaveM,
+                                   n0 + wn * Cfg::kWaveN, lane, split);
 }
 
 }  // namespace gemm
