@@ -94,11 +94,13 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 //    faster than the register-staged kernel at 4096^3 and on both M = 8192
 //    prefill shapes);
 //  * otherwise (M of a few hundred: the M = 256 decode layers, 512-row
-//    projections): register-staged 256 x 128 tiles, K split to about 256
-//    workgroups, rotation on.
+//    projections): direct-to-LDS 256 x 128 tiles with a three-slot ring, K
+//    split to about 256 workgroups, rotation on (at M = 256 0.5-6 % faster
+//    than the register-staged 256 x 128 tiles; with two slots 6-8 %
+//    slower, the loads of a step then have one step to land).
 constexpr int kCUs = 256;
 constexpr const char* kBig = "t256x256x64_w2x2_s2_x2_p8";
-constexpr const char* kRegStageMid = "t256x128x64_w2x2_s2_x2_p6";
+constexpr const char* kMid = "t256x128x64_w2x2_s3_x2_p8";
 constexpr const char* kSmallM32 = "t32x32x64_w1x1_s8_x2_p9";
 constexpr const char* kSmallM64 = "t64x32x64_w1x1_s6_x2_p9";
 constexpr const char* kSkinny32 = "t32x128x64_w1x4_s6_x2_p0";
@@ -175,7 +177,7 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
     p.splits = 1;
     p.k_rot = 0;
   } else {
-    p.tile = find_tile_config(kRegStageMid);
+    p.tile = find_tile_config(kMid);
     p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
     p.k_rot = 1;
   }

@@ -74,6 +74,9 @@
 #ifndef GEMM_INST_u
 #define GEMM_INST_u GEMM_NO_INST
 #endif
+#ifndef GEMM_INST_v
+#define GEMM_INST_v GEMM_NO_INST
+#endif
 
 
 namespace gemm {

@@ -31,6 +31,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -144,6 +145,38 @@ def tune_shape(M: int, N: int, K: int, half: bool = False, keep: int = 6,
             "first_pass": {p: round(t, 3) for p, t in sorted(first.items(), key=lambda x: x[1])[:20]}}
 
 
+def read_table(path: str) -> dict[tuple[int, int, int], str]:
+    """The entries of a table written by write_table (empty if none)."""
+    out = {}
+    try:
+        text = open(path).read()
+    except OSError:
+        return out
+    for line in text.splitlines():
+        m = re.match(r'^\{(\d+), (\d+), (\d+), "([^"]+)"\},$', line.strip())
+        if m:
+            out[(int(m.group(1)), int(m.group(2)), int(m.group(3)))] = m.group(4)
+    return out
+
+
+def choose_entries(results: dict, old: dict, min_gain: float) -> list[tuple[int, int, int, str]]:
+    """Table rows from a sweep's results.  The sweep times the plan the
+    library currently picks ("auto"), which for a shape already in the table
+    is that table entry, not the static rules.  So: a shape gets the sweep's
+    best plan if it beats the current choice by more than min_gain; else a
+    shape already in the table keeps its entry (still within min_gain of the
+    best); else the rules stay in charge."""
+    entries = []
+    for key, r in results.items():
+        M, N, K = (int(v) for v in key.split("x"))
+        auto, auto_us = r["auto"]
+        if r["best"] != auto and r["us"] < auto_us * (1 - min_gain):
+            entries.append((M, N, K, r["best"]))
+        elif (M, N, K) in old:
+            entries.append((M, N, K, old[(M, N, K)]))
+    return entries
+
+
 def write_table(entries: list[tuple[int, int, int, str]], path: str, note: str) -> None:
     """Write the C include the plan choice reads: one {M, N, K, "plan"} row
     per shape."""
@@ -168,7 +201,20 @@ def main(argv=None) -> int:
     ap.add_argument("--json", default=os.path.join(_HERE, "csrc", "gemm_tuned.json"))
     ap.add_argument("--min-gain", type=float, default=0.02,
                     help="keep a table entry only if it beats the rules by this fraction")
+    ap.add_argument("--from-json", default="",
+                    help="rebuild the table from a saved sweep (no GPU) instead of sweeping")
     args = ap.parse_args(argv)
+    old = read_table(args.out)
+
+    if args.from_json:
+        with open(args.from_json) as f:
+            saved = json.load(f)
+        entries = choose_entries(saved["results"], old, args.min_gain)
+        note = (f"{len(entries)} of {len(saved['results'])} swept shapes in the table, rebuilt "
+                f"from {os.path.basename(args.from_json)} (min gain {args.min_gain:.0%})")
+        write_table(entries, args.out, note)
+        print(note)
+        return 0
 
     import torch
 
@@ -191,15 +237,13 @@ def main(argv=None) -> int:
         if s:
             M, N, K = (int(v) for v in s.split("x"))
             shapes.append((M, N, K))
-    results, entries = {}, []
+    results = {}
     t0 = time.time()
     for (M, N, K) in shapes:
-        r = tune_shape(M, N, K)
-        results[f"{M}x{N}x{K}"] = r
-        if r["best"] != r["auto"][0] and r["us"] < r["auto"][1] * (1 - args.min_gain):
-            entries.append((M, N, K, r["best"]))
-    note = (f"{len(entries)} of {len(shapes)} shapes beat the rules by more than "
-            f"{args.min_gain:.0%}; sweep took {time.time() - t0:.0f} s")
+        results[f"{M}x{N}x{K}"] = tune_shape(M, N, K)
+    entries = choose_entries(results, old, args.min_gain)
+    note = (f"{len(entries)} of {len(shapes)} swept shapes in the table (min gain "
+            f"{args.min_gain:.0%}); sweep took {time.time() - t0:.0f} s")
     write_table(entries, args.out, note)
     with open(args.json, "w") as f:
         json.dump({"note": note, "results": results}, f, indent=1)

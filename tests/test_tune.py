@@ -69,3 +69,30 @@ def test_committed_table_entries_are_used(lib):
         cm = PLAN.match(chosen)
         assert cm.group(1) == pm.group(1) and cm.group(3) == pm.group(3), (plan, chosen)
         assert (cm.group(4) or "") == (pm.group(4) or ""), (plan, chosen)
+
+
+def test_choose_entries_keeps_still_best_table_rows():
+    """The sweep times the current choice, which for a tabled shape is its
+    table row: a row that is still the best is kept, a better plan replaces
+    it, and an untabled shape enters only with a gain over the rules."""
+    from dense_gemm_bf16_amd.tune import choose_entries
+
+    old = {(1, 2, 3): "p_old", (4, 5, 6): "q_old"}
+    results = {
+        "1x2x3": {"best": "p_old", "us": 10.0, "auto": ["p_old", 10.0]},
+        "4x5x6": {"best": "q_new", "us": 9.0, "auto": ["q_old", 10.0]},
+        "7x8x9": {"best": "r_new", "us": 9.9, "auto": ["r_rule", 10.0]},
+        "9x9x9": {"best": "s_new", "us": 9.0, "auto": ["s_rule", 10.0]},
+    }
+    got = choose_entries(results, old, 0.02)
+    assert got == [(1, 2, 3, "p_old"), (4, 5, 6, "q_new"), (9, 9, 9, "s_new")]
+
+
+def test_read_table_round_trip(tmp_path):
+    from dense_gemm_bf16_amd.tune import read_table, write_table
+
+    out = tmp_path / "t.inc"
+    rows = [(1, 8192, 8192, "t32x32x64_w1x1_s8_x2_p9_k1_g4_r1"), (512, 512, 512, "t64x128x64_w1x4_s6_x2_p0_k1_g8")]
+    write_table(rows, str(out), "note")
+    assert read_table(str(out)) == {(M, N, K): p for M, N, K, p in rows}
+    assert read_table(str(tmp_path / "missing.inc")) == {}
