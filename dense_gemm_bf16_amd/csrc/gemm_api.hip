@@ -93,14 +93,21 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 //    the direct-to-LDS 256 x 256 x 64 kernel, no split (at steady clock 6 %
 //    faster than the register-staged kernel at 4096^3 and on both M = 8192
 //    prefill shapes);
-//  * otherwise (M of a few hundred: the M = 256 decode layers, 512-row
-//    projections): direct-to-LDS 256 x 128 tiles with a three-slot ring, K
-//    split to about 256 workgroups, rotation on (at M = 256 0.5-6 % faster
-//    than the register-staged 256 x 128 tiles; with two slots 6-8 %
-//    slower, the loads of a step then have one step to land).
+//  * otherwise direct-to-LDS 256 x 128 tiles with a three-slot ring (0.5-6 %
+//    faster than the register-staged 256 x 128 tiles at M = 256; with two
+//    slots 6-8 % slower, a step's loads then have one step to land),
+//    rotation on for a single row of tiles, K split to about 256
+//    workgroups -- unless they would need
+//    a split while 128 x 128 tiles fill the chip without one (M = 512, N =
+//    8192: 44 vs 52 us; 1024 x 4096 x 4096: 35 vs 43 us), or the split
+//    leaves fewer than 24 K-steps per slice, where first loads and partial
+//    stores weigh more than the smaller tile costs (512 x 4096 x 4096: 128 x
+//    128 split 2, 26.5 vs 28.6 us).  Then direct-to-LDS 128 x 128 tiles with
+//    a four-slot ring, split to about 256 workgroups.
 constexpr int kCUs = 256;
 constexpr const char* kBig = "t256x256x64_w2x2_s2_x2_p8";
 constexpr const char* kMid = "t256x128x64_w2x2_s3_x2_p8";
+constexpr const char* kMid128 = "t128x128x64_w2x2_s4_x2_p8";
 constexpr const char* kSmallM32 = "t32x32x64_w1x1_s8_x2_p9";
 constexpr const char* kSmallM64 = "t64x32x64_w1x1_s6_x2_p9";
 constexpr const char* kSkinny32 = "t32x128x64_w1x4_s6_x2_p0";
@@ -177,9 +184,22 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
     p.splits = 1;
     p.k_rot = 0;
   } else {
-    p.tile = find_tile_config(kMid);
-    p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
-    p.k_rot = 1;
+    const TileConfig* mid = find_tile_config(kMid);
+    const TileConfig* m128 = find_tile_config(kMid128);
+    const int64_t k_tiles = (K + mid->bk - 1) / mid->bk;
+    const int mid_splits = choose_splits(tiles_of(mid, M, N), k_tiles);
+    if (mid_splits == 1 || (tiles_of(m128, M, N) < kCUs - kCUs / 8 && k_tiles / mid_splits >= 24)) {
+      p.tile = mid;
+      p.splits = mid_splits;
+      // rotation only for a single row of tiles: with several, the tiles
+      // that share a B panel read it together from L2 when unrotated
+      // (1024 x 8192 x 8192: 117 vs 128 us)
+      p.k_rot = (M + mid->bm - 1) / mid->bm == 1 ? 1 : 0;
+    } else {
+      p.tile = m128;
+      p.splits = choose_splits(tiles_of(m128, M, N), k_tiles);
+      p.k_rot = 0;
+    }
   }
   finish_plan(&p, M, N, K);
   return p;

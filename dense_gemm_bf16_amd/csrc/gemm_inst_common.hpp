@@ -77,6 +77,9 @@
 #ifndef GEMM_INST_v
 #define GEMM_INST_v GEMM_NO_INST
 #endif
+#ifndef GEMM_INST_w
+#define GEMM_INST_w GEMM_NO_INST
+#endif
 
 
 namespace gemm {

@@ -125,6 +125,7 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t128x256x64_w2x2_s2_x2_p6, 128, 256, 64, 2, 2, 2, 2, 6, 1, s) \
   X(t256x256x64_w2x2_s2_x2_p8, 256, 256, 64, 2, 2, 2, 2, 8, 1, t) \
   X(t256x128x64_w2x2_s3_x2_p8, 256, 128, 64, 2, 2, 3, 2, 8, 1, v) \
+  X(t128x128x64_w2x2_s4_x2_p8, 128, 128, 64, 2, 2, 4, 2, 8, 1, w) \
   X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 1, u)     \
   X(t64x32x64_w1x1_s6_x2_p9, 64, 32, 64, 1, 1, 6, 2, 9, 1, u)     \
   X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, 0, j) \
