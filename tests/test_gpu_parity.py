@@ -211,7 +211,9 @@ def test_empty_m_or_n_is_noop():
 
 
 def test_split_k_matches_unsplit_on_integers():
-    """Decode shape with integer inputs: split and unsplit both bit-exact."""
+    """Decode shape with integer inputs: split and unsplit both bit-exact,
+    for every slice count the reduction has a fixed-count kernel for (2-8)
+    and for one beyond (16, the run-time count loop)."""
     M, N, K = 256, 1024, 8192
     A = int_bf16(M, K, seed=600)
     B = int_bf16(N, K, seed=601)
@@ -219,7 +221,7 @@ def test_split_k_matches_unsplit_on_integers():
 
     ref16, _ = _oracle().gemm(A, B)
     tile = g.config_name(M, N, K).split("_k")[0]
-    for cfg in [f"{tile}_k1", f"{tile}_k8", f"{tile}_k5"]:
+    for cfg in [f"{tile}_k{k}" for k in (1, 2, 3, 4, 5, 6, 7, 8, 16)]:
         got = run_gemm(A, B, config=cfg)
         assert check_bf16(got, ref16, None, K, exact=True)["ok"], cfg
 
