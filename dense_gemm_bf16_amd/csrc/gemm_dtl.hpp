@@ -17,7 +17,8 @@
 // Per K-step X (SUB = BK/16 substeps), in every wave:
 //   substep kk < SUB-1:  MFMAs of kk with, between them, the ds_reads of
 //                        substep kk+1's fragments and load group kk+1 of
-//                        step X+S-1 (groups 1..F-1; F = 2 groups per step);
+//                        step X+S-1 (groups 1..F-1; F = 2 groups per step
+//                        with two slots, SUB with three or more);
 //   substep SUB-1:       wait for step X+1's loads, barrier (this also frees
 //                        slot X % S: every wave has read its last fragments
 //                        of step X), then the MFMAs of substep SUB-1 with the
@@ -52,7 +53,11 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   constexpr int SUB = Cfg::kSub;
   constexpr int LA = Cfg::kLoadsA;
   constexpr int L = Cfg::kLoadsPerStage;
-  constexpr int F = 2;  // load groups per step
+  // Load groups per step.  With two slots a step's loads must land within
+  // the step before it, so they go out in the first two substeps; with
+  // three or more they have over a step to land and are spread over all
+  // four, which keeps fewer loads between any two MFMAs.
+  constexpr int F = (S >= 3 && Cfg::kLoadsPerStage % Cfg::kSub == 0) ? Cfg::kSub : 2;
   constexpr int kStore = store_kind<FLAGS>();
   constexpr bool kHalf = (FLAGS & kF16) != 0;
   constexpr bool kSplit = (FLAGS & kSplitK) != 0;
