@@ -425,11 +425,13 @@ int gemm_bf16_release_workspace(void) {
   for (gemm::Workspace& w : gemm::g_ws) {
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) cur = w.device;
-    hipSetDevice(w.device);
-    hipError_t e = hipStreamSynchronize(w.stream);
+    hipError_t e = hipSetDevice(w.device);
+    if (e == hipSuccess) e = hipStreamSynchronize(w.stream);
     if (e == hipSuccess) e = hipFree(w.ptr);
     if (e != hipSuccess) rc = gemm::hip_fail(e);
-    hipSetDevice(cur);
+    // restore the caller's device; a failure here is reported like the rest
+    e = hipSetDevice(cur);
+    if (e != hipSuccess) rc = gemm::hip_fail(e);
   }
   gemm::g_ws.clear();
   return rc;

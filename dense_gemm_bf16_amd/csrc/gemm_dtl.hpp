@@ -217,7 +217,6 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   auto step = [&](auto vc, int X) __attribute__((always_inline)) {
     constexpr int V = decltype(vc)::value;
     const lds_u8* sa = smem + (X % S) * Cfg::kStageBytes;
-    const lds_u8* sb = sa + Cfg::kABytes;
     constexpr_for<SUB>([&](auto kc_) __attribute__((always_inline)) {
       constexpr int kk = decltype(kc_)::value;
       constexpr int cur = kk & 1, nxt = cur ^ 1;

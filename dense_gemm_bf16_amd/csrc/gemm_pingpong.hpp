@@ -55,7 +55,6 @@ gemm_bf16_pingpong_kernel(KernelArgs a) {
   constexpr int T = Cfg::kThreads;
   constexpr int CPR = Cfg::kCpr;
   constexpr int LPS = Cfg::kLoadsPerStage;
-  constexpr int LA = Cfg::kLoadsA;
   constexpr int SUB = Cfg::kSub;
   constexpr int kStore = store_kind<FLAGS>();
   constexpr bool kHalf = (FLAGS & kF16) != 0;
