@@ -246,3 +246,29 @@ def test_identity_and_k1_closed_forms():
     b = normal_bf16(30, 1, seed=702)
     ref16, _ = _oracle().gemm(a, b)
     assert np.array_equal(run_gemm(a, b, K=1), ref16)
+
+
+def test_random_shapes_automatic_plan_bit_exact():
+    """Forty seeded random shapes (M, N log-uniform in [1, 3000], K in
+    [1, 4000], almost all ragged), integer inputs, through the automatic
+    plan: every shape rule, split count and edge path the choice reaches
+    must be bit-exact."""
+    import dense_gemm_bf16_amd as g
+
+    rng = np.random.default_rng(4242)
+    o = _oracle()
+    plans = set()
+    for i in range(40):
+        M = int(np.exp(rng.uniform(0, np.log(3000))))
+        N = int(np.exp(rng.uniform(0, np.log(3000))))
+        K = int(np.exp(rng.uniform(0, np.log(4000))))
+        A = int_bf16(M, K, seed=900 + 2 * i)
+        B = int_bf16(N, K, seed=901 + 2 * i)
+        ref16, _ = o.gemm(A, B)
+        got = run_gemm(A, B)
+        rep = check_bf16(got, ref16, None, K, exact=True)
+        plan = g.config_name(M, N, K)
+        plans.add(plan.split("_k")[0])
+        print(i, (M, N, K), plan, rep, flush=True)
+        assert rep["ok"], ((M, N, K), plan, rep)
+    print("tiles used:", sorted(plans), flush=True)
