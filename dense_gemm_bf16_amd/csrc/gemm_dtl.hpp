@@ -1,7 +1,9 @@
 // Direct-to-LDS GEMM kernel: operand tiles go from global memory straight
 // into an S-slot LDS ring with LDS-DMA loads (`buffer_load_dwordx4 ... lds`,
-// no VGPR staging and no ds_write), each wave computes a 32-aligned block of
-// the tile from ds_read_b128 fragments with 32x32x16 MFMAs.
+// no VGPR staging and no ds_write), each wave computes a block of the tile
+// from ds_read_b128 fragments with 32x32x16 MFMAs (MF = 32) or 16x16x32
+// MFMAs (MF = 16; same work per cycle, and the chip holds a higher clock
+// under its power limit with them).
 //
 // Why this shape of kernel, from measurements on MI355X:
 //  * LDS writes through ds_write_b128 run at ~76-105 B/clk per CU, LDS reads
@@ -14,7 +16,8 @@
 //  * The per-CU load path delivers ~64 B/clk; a 256 x 256 tile needs 32 B per
 //    MFMA-clock at full rate, so loads keep up.
 //
-// Per K-step X (SUB = BK/16 substeps), in every wave:
+// Per K-step X (SUB = BK/16 substeps of 32x32x16 MFMAs, or BK/32 of
+// 16x16x32), in every wave:
 //   substep kk < SUB-1:  MFMAs of kk with, between them, the ds_reads of
 //                        substep kk+1's fragments and load group kk+1 of
 //                        step X+S-1 (groups 1..F-1; F = 2 groups per step
@@ -24,6 +27,10 @@
 //                        of step X), then the MFMAs of substep SUB-1 with the
 //                        reads of step X+1's first fragments and group 0 of
 //                        step X+S (into the slot just freed) between them.
+//                        With two substeps (16x16x32, BK = 64) the first half
+//                        of this substep's MFMAs runs before the barrier, so
+//                        that it still sits three quarters into the step and
+//                        the loads have as long to land as with four.
 // So a load is issued S-2 steps and a few substeps before the barrier that
 // needs it, and nothing waits on a load issued in the same step unless S = 2.
 //
@@ -43,11 +50,11 @@
 
 namespace gemm {
 
-template <int BM, int BN, int BK, int WM, int WN, int S, int SWZ, int FLAGS>
+template <int BM, int BN, int BK, int WM, int WN, int S, int SWZ, int FLAGS, int MF>
 __global__ __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                           amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void
 gemm_bf16_dtl_kernel(KernelArgs a) {
-  using Cfg = TileCfg<BM, BN, BK, WM, WN, S, SWZ>;
+  using Cfg = TileCfg<BM, BN, BK, WM, WN, S, SWZ, MF>;
   constexpr int T = Cfg::kThreads;
   constexpr int CPR = Cfg::kCpr;
   constexpr int SUB = Cfg::kSub;
@@ -181,14 +188,20 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
     ring_wait_barrier_n<L, S - 2>(later);
   };
 
-  f32x16 acc[Cfg::kFragM][Cfg::kFragN];
+  typename Cfg::Acc acc[Cfg::kFragM][Cfg::kFragN];
 #pragma unroll
   for (int i = 0; i < Cfg::kFragM; ++i)
 #pragma unroll
     for (int j = 0; j < Cfg::kFragN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  bf16x8 fa[2][Cfg::kFragM], fb[2][Cfg::kFragN];
+      for (int r = 0; r < MF * MF / 64; ++r) acc[i][j][r] = 0.0f;
+  if constexpr (MF == 16) mfma16_settle();
+  // B fragments alternate between two buffers per substep.  A fragments
+  // too with 32 x 32 blocks; with 16 x 16 blocks (twice as many fragments)
+  // there is one A buffer, and fragment fm of the next substep replaces
+  // that of the current one as soon as its row of MFMAs has issued.
+  constexpr int kABufs = MF == 16 ? 1 : 2;
+  bf16x8 fa[kABufs][Cfg::kFragM], fb[2][Cfg::kFragN];
 
   // ---- prologue: steps 0..S-2 whole, group 0 of step S-1 -------------------
   constexpr int G = L / F;
@@ -230,28 +243,88 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
       const lds_u8* ra = kLast ? smem + ((X + 1) % S) * Cfg::kStageBytes : sa;
       constexpr int rkk = kLast ? 0 : kk + 1;
       const bool reads = !kLast || V <= 1 || X + 1 < n_iter;
+      // MFMAs of this substep that run before the barrier (kLast only)
+      constexpr int NM = Cfg::kFragM * Cfg::kFragN;
+      constexpr int J0 = kLast && SUB == 2 ? NM / 2 : 0;
+      constexpr int ca = MF == 16 ? 0 : cur, na = MF == 16 ? 0 : nxt;  // A buffers
       if constexpr (kLast) {
+        if constexpr (J0 > 0) {
+          if constexpr (MF == 16)
+            mfma_each<Cfg, kHalf, 0, J0>(acc, fa[ca], fb[cur], [](auto) {});
+          else
+            mfma_range<Cfg, kHalf, 0, J0, 0>(acc, fa[ca], fb[cur], [](auto) {});
+          // MFMAs touch no memory, so without this the scheduler would move
+          // them past the barrier
+          __builtin_amdgcn_sched_barrier(0);
+        }
         // in flight after step X+1: steps X+2 .. min(X+S-1, n_iter-1)
         if (reads) publish(X + 1, V <= 1 ? S - 2 : min(S - 2, n_iter - 2 - X));
+        if constexpr (J0 > 0) __builtin_amdgcn_sched_barrier(0);
       }
-      // The reads (in the order the next substep needs them) and the loads
-      // alternate between the MFMAs, evenly: issued back to back, the reads
-      // of four waves leaving a barrier together queue in the LDS ahead of
-      // their MFMAs, and a burst of loads fills the texture path.
-      constexpr int NR = Cfg::kFragM + Cfg::kFragN;
       constexpr int NL = kLoads ? G : 0;
-      mfma_interleave<Cfg, kHalf, NR + NL>(
-          acc, fa[cur], fb[cur], [&](auto qc) __attribute__((always_inline)) {
-            constexpr int p = decltype(qc)::value;
-            constexpr int rb = p * NR / (NR + NL), rn = (p + 1) * NR / (NR + NL);
-            if constexpr (rn > rb) {
-              if (reads)
-                read_frag_one<Cfg, SWZ, frag_need_order<Cfg>(rb)>(ra, ra + Cfg::kABytes, rkk, wm,
-                                                                  wn, lane, fa[nxt], fb[nxt]);
-            } else {
-              dma_one(Y, grp * G + (p - rb));
-            }
-          });
+      if constexpr (MF == 16) {
+        // Where each operation goes (after which MFMA j of the substep; j
+        // counts fm-major).  Substep 0 issues its loads (the group that
+        // must land by this step's barrier) in its first half, i.e. the
+        // first quarter of the step as with 32 x 32 blocks: at the clock
+        // these MFMAs run at, a step is short enough that loads spread
+        // further stall the barrier.  A fragment i of the next substep may
+        // replace the current one only after MFMA i*FN + FN-1, the last of
+        // row i.  Row 0 of the next substep needs A fragment 0 and every B
+        // fragment, so those are read first: in substep 0 the B fragments
+        // over its middle half, in the last substep (where reads wait for
+        // the barrier, and the loads, a step ahead, are spread over the
+        // rest) A0, B0 .. B(FN-1), A1, ... evenly over the MFMAs after it.
+        constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN, NR = FM + FN, n = NM - J0;
+        auto pos_a = [](int i) constexpr {
+          const int row_end = i * FN + FN - 1;
+          const int want = kLast ? J0 + ((i == 0 ? 0 : FN + i) * n) / NR : row_end;
+          return want > row_end ? want : row_end;
+        };
+        auto pos_b = [](int i) constexpr {
+          return kLast ? J0 + ((1 + i) * n) / NR : n / 4 + (i * n) / (2 * FN);
+        };
+        constexpr int load_span = kLast ? n : n / 2;
+        mfma_each<Cfg, kHalf, J0, NM>(
+            acc, fa[0], fb[cur], [&](auto jc) __attribute__((always_inline)) {
+              constexpr int j = decltype(jc)::value;
+              constexpr_for<NR>([&](auto rc) __attribute__((always_inline)) {
+                constexpr int r = decltype(rc)::value;  // A fragments, then B
+                constexpr int at = r < FM ? pos_a(r) : pos_b(r - FM);
+                if constexpr ((at < NM - 1 ? at : NM - 1) == j) {
+                  if (reads)
+                    read_frag_one<Cfg, SWZ, r>(ra, ra + Cfg::kABytes, rkk, wm, wn, lane, fa[0],
+                                               fb[nxt]);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              });
+              constexpr_for<NL>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                if constexpr (J0 + ((2 * q + 1) * load_span) / (2 * NL) == j) {
+                  dma_one(Y, grp * G + q);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              });
+            });
+      } else {
+        // The reads (in the order the next substep needs them) and the loads
+        // alternate between the MFMAs, evenly: issued back to back, the
+        // reads of four waves leaving a barrier together queue in the LDS
+        // ahead of their MFMAs, and a burst of loads fills the texture path.
+        constexpr int NR = Cfg::kFragM + Cfg::kFragN;
+        mfma_range<Cfg, kHalf, J0, NM, NR + NL>(
+            acc, fa[ca], fb[cur], [&](auto qc) __attribute__((always_inline)) {
+              constexpr int p = decltype(qc)::value;
+              constexpr int rb = p * NR / (NR + NL), rn = (p + 1) * NR / (NR + NL);
+              if constexpr (rn > rb) {
+                if (reads)
+                  read_frag_one<Cfg, SWZ, frag_need_order<Cfg>(rb)>(
+                      ra, ra + Cfg::kABytes, rkk, wm, wn, lane, fa[na], fb[nxt]);
+              } else {
+                dma_one(Y, grp * G + (p - rb));
+              }
+            });
+      }
     });
   };
 
@@ -263,6 +336,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   }
   for (; X < n_iter; ++X) step(std::integral_constant<int, 2>{}, X);
 
+  if constexpr (MF == 16) mfma16_settle();
   finish_tile<Cfg, kStore, kSplit>(a, smem, wave, m0, n0, acc, m0 + wm * Cfg::kWaveM,
                                    n0 + wn * Cfg::kWaveN, lane, split);
 }

@@ -80,6 +80,15 @@
 #ifndef GEMM_INST_w
 #define GEMM_INST_w GEMM_NO_INST
 #endif
+#ifndef GEMM_INST_x
+#define GEMM_INST_x GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_y
+#define GEMM_INST_y GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_z
+#define GEMM_INST_z GEMM_NO_INST
+#endif
 
 
 namespace gemm {

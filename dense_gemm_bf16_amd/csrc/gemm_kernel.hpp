@@ -244,26 +244,40 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 //          16 rows of a phase cover 16 distinct (row-in-256-bytes, chunk)
 //          pairs.  128-byte rows: (row ^ row/8) mod 8; 64-byte rows:
 //          (row / 4) mod 4.
+//   SWZ 3: 128-byte rows: (row ^ (row/8) mod 2) mod 8, the same as SWZ 2
+//          on rows 0..15 but repeating every 16 rows, so just as
+//          conflict-free, and every 16- or 32-row fragment of a wave sees
+//          the same pattern: their read addresses differ by constants only.
 template <int SWZ, int CPR>
 __host__ __device__ constexpr int swz(int row) {
   if constexpr (SWZ == 0) return 0;
   else if constexpr (SWZ == 1) return row & (CPR - 1);
+  else if constexpr (CPR == 8 && SWZ == 3) return (row ^ ((row >> 3) & 1)) & 7;
   else if constexpr (CPR == 8) return (row ^ (row >> 3)) & 7;
   else return (row >> 2) & 3;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int SWZ>
+// MF is the MFMA block: 32 (v_mfma_f32_32x32x16, 16 of K per instruction,
+// 16 accumulators per lane) or 16 (v_mfma_f32_16x16x32, 32 of K, 4
+// accumulators per lane).  Both do the same work per cycle; under the power
+// limit a stream of 16x16x32 MFMAs holds a higher clock (measured on MI355X:
+// 1.86 vs 1.61 GHz, one wave per SIMD, random bf16 operands).
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int SWZ, int MF = 32>
 struct TileCfg {
+  static_assert(MF == 32 || MF == 16, "32x32x16 or 16x16x32 MFMA blocks");
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int kBM = BM;
   static constexpr int kBN = BN;
+  static constexpr int kMf = MF;          // rows (and columns) of one MFMA block
+  static constexpr int kMfK = 512 / MF;   // K of one MFMA
   static constexpr int kWaveM = BM / WAVES_M;
   static constexpr int kWaveN = BN / WAVES_N;
-  static constexpr int kFragM = kWaveM / 32;
-  static constexpr int kFragN = kWaveN / 32;
+  static constexpr int kFragM = kWaveM / MF;
+  static constexpr int kFragN = kWaveN / MF;
   static constexpr int kRowBytes = BK * 2;
-  static constexpr int kCpr = BK / 8;   // 16-byte chunks per LDS row
-  static constexpr int kSub = BK / 16;  // 16-wide MFMA substeps per K-step
+  static constexpr int kCpr = BK / 8;      // 16-byte chunks per LDS row
+  static constexpr int kSub = BK / kMfK;   // MFMA substeps per K-step
+  using Acc = std::conditional_t<MF == 32, f32x16, f32x4>;  // one block's accumulators
   static constexpr int kABytes = BM * kRowBytes;
   static constexpr int kBBytes = BN * kRowBytes;
   static constexpr int kStageBytes = kABytes + kBBytes;
@@ -272,7 +286,7 @@ struct TileCfg {
   static constexpr int kLoadsB = kBBytes / (kThreads * 16);
   static constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
   static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
-  static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile in 32-blocks");
+  static_assert(kWaveM % MF == 0 && kWaveN % MF == 0, "wave tile in MFMA blocks");
   static_assert(kABytes % (kThreads * 16) == 0, "A tile splits into loads");
   static_assert(kBBytes % (kThreads * 16) == 0, "B tile splits into loads");
   static_assert(kLdsBytes <= 160 * 1024, "LDS is 160 KB per CU");
@@ -335,39 +349,66 @@ __device__ __forceinline__ void fix_tail_chunks(lds_u8* dst, const int (&chunk)[
 
 // --------------------------------------------------------------- fragments
 
-// Read the MFMA fragments of one 16-wide K substep from a ring slot.
-// Lane l supplies 8 consecutive k of row (l % 32) at 16-byte chunk
-// 2*kk + l/32 of that row.
+// Read the MFMA fragments of one K substep (kMfK wide) from a ring slot.
+// Lane l supplies 8 consecutive k of row (l % MF) at 16-byte chunk
+// (kMfK / 8) * kk + l / MF of that row: for 32x32x16 blocks the two lane
+// halves take the two 8-wide halves of the substep, for 16x16x32 blocks the
+// four lane quarters its four 8-wide quarters.
 template <typename Cfg, int SWZ>
 __device__ __forceinline__ void read_frags(const lds_u8* sa, const lds_u8* sb, int kk, int wm,
                                            int wn, int lane, bf16x8 (&fa)[Cfg::kFragM],
                                            bf16x8 (&fb)[Cfg::kFragN]) {
   typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
-  constexpr int R = Cfg::kRowBytes, CPR = Cfg::kCpr;
-  const int lrow = lane & 31, lhalf = lane >> 5;
+  constexpr int R = Cfg::kRowBytes, CPR = Cfg::kCpr, MF = Cfg::kMf;
+  const int lrow = lane % MF, chunk = (Cfg::kMfK / 8) * kk + lane / MF;
 #pragma unroll
   for (int fm = 0; fm < Cfg::kFragM; ++fm) {
-    const int row = wm * Cfg::kWaveM + fm * 32 + lrow;
-    fa[fm] = *(lds_frag*)(sa + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
+    const int row = wm * Cfg::kWaveM + fm * MF + lrow;
+    fa[fm] = *(lds_frag*)(sa + row * R + ((chunk ^ swz<SWZ, CPR>(row)) << 4));
   }
 #pragma unroll
   for (int fn = 0; fn < Cfg::kFragN; ++fn) {
-    const int row = wn * Cfg::kWaveN + fn * 32 + lrow;
-    fb[fn] = *(lds_frag*)(sb + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
+    const int row = wn * Cfg::kWaveN + fn * MF + lrow;
+    fb[fn] = *(lds_frag*)(sb + row * R + ((chunk ^ swz<SWZ, CPR>(row)) << 4));
   }
 }
 
-// One 32 x 32 x 16 MFMA, D[n][m] += sum_k B[n][k] * A[m][k] (first operand
-// from B, second from A).  The fragments hold raw 16-bit patterns; HALF
-// reads them as fp16, otherwise as bf16.
+// One MFMA, D[n][m] += sum_k B[n][k] * A[m][k] (first operand from B, second
+// from A): 32 x 32 x 16 on a 16-float accumulator block, 16 x 16 x 32 on a
+// 4-float one.  The fragments hold raw 16-bit patterns; HALF reads them as
+// fp16, otherwise as bf16.
 template <bool HALF>
-__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& b, const bf16x8& a,
-                                                const f32x16& c) {
+__device__ __forceinline__ f32x16 mfma_op(const bf16x8& b, const bf16x8& a, const f32x16& c) {
   if constexpr (HALF)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, b),
                                                   __builtin_bit_cast(f16x8, a), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+}
+// The 16 x 16 x 32 form is written as asm with the accumulator tied in
+// AGPRs: with the builtin, the compiler gave some of a 128 x 128 wave tile's
+// 64 MFMAs a destination other than their accumulator input, and with all
+// 256 AGPRs holding accumulators it then shuffled blocks through VGPRs
+// every K-step.  The compiler cannot see the MFMA's latency through asm,
+// so callers separate the accumulators' VALU writes before the first and
+// reads after the last of these MFMAs by mfma16_settle().
+template <bool HALF>
+__device__ __forceinline__ f32x4 mfma_op(const bf16x8& b, const bf16x8& a, const f32x4& c) {
+  f32x4 d = c;
+  if constexpr (HALF)
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(b), "v"(a));
+  else
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(b), "v"(a));
+  return d;
+}
+
+// Wait states between VALU accesses of accumulators and the asm MFMAs
+// above (a 4-pass MFMA's result is readable 18 wait states after issue;
+// 32 here), fenced so the scheduler moves nothing across.
+__device__ __forceinline__ void mfma16_settle() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // The order in which the MFMAs of a substep (fm-major, fn inner) first use
@@ -398,27 +439,26 @@ __device__ __forceinline__ void read_frag_one(const lds_u8* sa, const lds_u8* sb
                                               int wn, int lane, bf16x8 (&fa)[Cfg::kFragM],
                                               bf16x8 (&fb)[Cfg::kFragN]) {
   typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
-  constexpr int R = Cfg::kRowBytes, CPR = Cfg::kCpr;
-  const int lrow = lane & 31, lhalf = lane >> 5;
+  constexpr int R = Cfg::kRowBytes, CPR = Cfg::kCpr, MF = Cfg::kMf;
+  const int lrow = lane % MF, chunk = (Cfg::kMfK / 8) * kk + lane / MF;
   if constexpr (IDX < Cfg::kFragM) {
-    const int row = wm * Cfg::kWaveM + IDX * 32 + lrow;
-    fa[IDX] = *(lds_frag*)(sa + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
+    const int row = wm * Cfg::kWaveM + IDX * MF + lrow;
+    fa[IDX] = *(lds_frag*)(sa + row * R + ((chunk ^ swz<SWZ, CPR>(row)) << 4));
   } else {
-    const int row = wn * Cfg::kWaveN + (IDX - Cfg::kFragM) * 32 + lrow;
-    fb[IDX - Cfg::kFragM] =
-        *(lds_frag*)(sb + row * R + (((2 * kk + lhalf) ^ swz<SWZ, CPR>(row)) << 4));
+    const int row = wn * Cfg::kWaveN + (IDX - Cfg::kFragM) * MF + lrow;
+    fb[IDX - Cfg::kFragM] = *(lds_frag*)(sb + row * R + ((chunk ^ swz<SWZ, CPR>(row)) << 4));
   }
 }
 
 template <typename Cfg, bool HALF>
-__device__ __forceinline__ void mfma_block(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+__device__ __forceinline__ void mfma_block(typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                            const bf16x8 (&fa)[Cfg::kFragM],
                                            const bf16x8 (&fb)[Cfg::kFragN]) {
 #pragma unroll
   for (int fm = 0; fm < Cfg::kFragM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Cfg::kFragN; ++fn)
-      acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
+      acc[fm][fn] = mfma_op<HALF>(fb[fn], fa[fm], acc[fm][fn]);
 }
 
 // Call f(std::integral_constant<int, i>) for i = 0 .. N-1 in order.
@@ -459,14 +499,14 @@ __device__ __forceinline__ void constexpr_for_window(int w, Fn&& f) {
 // goes after MFMA ceil((q+1)*n/G) - 1, and a scheduling barrier keeps each
 // load at its place in the MFMA stream.
 template <typename Cfg, bool HALF, int G, typename Dma>
-__device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+__device__ __forceinline__ void mfma_block_dma(typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                const bf16x8 (&fa)[Cfg::kFragM],
                                                const bf16x8 (&fb)[Cfg::kFragN], Dma&& dma) {
   constexpr int n = Cfg::kFragM * Cfg::kFragN;
 #pragma unroll
   for (int j = 0; j < n; ++j) {
     const int fm = j / Cfg::kFragN, fn = j % Cfg::kFragN;
-    acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
+    acc[fm][fn] = mfma_op<HALF>(fb[fn], fa[fm], acc[fm][fn]);
 #pragma unroll
     for (int q = (j * G) / n; q < ((j + 1) * G) / n; ++q) {
       dma(q);
@@ -475,24 +515,47 @@ __device__ __forceinline__ void mfma_block_dma(f32x16 (&acc)[Cfg::kFragM][Cfg::k
   }
 }
 
-// The MFMAs of one substep with G operations spaced evenly between them
-// (op q right after MFMA j for q in [j*G/n, (j+1)*G/n), so several per MFMA
-// when G > n), each pinned in place by a scheduling barrier.
-template <typename Cfg, bool HALF, int G, int J = 0, typename Op>
-__device__ __forceinline__ void mfma_interleave(f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                                const bf16x8 (&fa)[Cfg::kFragM],
-                                                const bf16x8 (&fb)[Cfg::kFragN], Op&& op) {
-  constexpr int n = Cfg::kFragM * Cfg::kFragN;
-  if constexpr (J < n) {
+// MFMAs J0 .. J1-1 of one substep (fm-major, fn inner) with G operations
+// spaced evenly between them (op q right after the j-th of them for q in
+// [j*G/n, (j+1)*G/n), n = J1 - J0, so several per MFMA when G > n), each
+// pinned in place by a scheduling barrier.
+template <typename Cfg, bool HALF, int J0, int J1, int G, int J = J0, typename Op>
+__device__ __forceinline__ void mfma_range(typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                           const bf16x8 (&fa)[Cfg::kFragM],
+                                           const bf16x8 (&fb)[Cfg::kFragN], Op&& op) {
+  constexpr int n = J1 - J0;
+  if constexpr (J < J1) {
     constexpr int fm = J / Cfg::kFragN, fn = J % Cfg::kFragN;
-    acc[fm][fn] = mfma_32x32x16<HALF>(fb[fn], fa[fm], acc[fm][fn]);
-    constexpr int qlo = (J * G) / n, qhi = ((J + 1) * G) / n;
+    acc[fm][fn] = mfma_op<HALF>(fb[fn], fa[fm], acc[fm][fn]);
+    constexpr int qlo = ((J - J0) * G) / n, qhi = ((J - J0 + 1) * G) / n;
     constexpr_for<qhi - qlo>([&](auto qc) __attribute__((always_inline)) {
       op(std::integral_constant<int, qlo + decltype(qc)::value>{});
       __builtin_amdgcn_sched_barrier(0);
     });
-    mfma_interleave<Cfg, HALF, G, J + 1>(acc, fa, fb, op);
+    mfma_range<Cfg, HALF, J0, J1, G, J + 1>(acc, fa, fb, op);
   }
+}
+
+// MFMAs J0 .. J1-1 of one substep (fm-major, fn inner), calling
+// after(std::integral_constant<int, j>) after MFMA j.
+template <typename Cfg, bool HALF, int J0, int J1, int J = J0, typename After>
+__device__ __forceinline__ void mfma_each(typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                          const bf16x8 (&fa)[Cfg::kFragM],
+                                          const bf16x8 (&fb)[Cfg::kFragN], After&& after) {
+  if constexpr (J < J1) {
+    constexpr int fm = J / Cfg::kFragN, fn = J % Cfg::kFragN;
+    acc[fm][fn] = mfma_op<HALF>(fb[fn], fa[fm], acc[fm][fn]);
+    after(std::integral_constant<int, J>{});
+    mfma_each<Cfg, HALF, J0, J1, J + 1>(acc, fa, fb, after);
+  }
+}
+
+// All MFMAs of one substep with G operations spaced evenly between them.
+template <typename Cfg, bool HALF, int G, typename Op>
+__device__ __forceinline__ void mfma_interleave(typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                const bf16x8 (&fa)[Cfg::kFragM],
+                                                const bf16x8 (&fb)[Cfg::kFragN], Op&& op) {
+  mfma_range<Cfg, HALF, 0, Cfg::kFragM * Cfg::kFragN, G>(acc, fa, fb, op);
 }
 
 // True if swz(i*RPI + r) == swz((i & 1)*RPI + r) for all i < n, r < RPI.
@@ -543,32 +606,42 @@ __device__ __forceinline__ void store_quad(void* Cbase, int64_t ld, const f32x4&
   }
 }
 
-// Store one 32 x 32 accumulator block whose rows start at m0 and columns at
-// n0: lane l holds row m0 + l % 32, columns n0 + 8g + 4(l / 32) .. +3 in
-// elements 4g .. 4g+3 (g = 0..3).  Rows >= M and columns >= N are skipped.
-template <int OUT>
-__device__ __forceinline__ void store_block(void* Cbase, int64_t ld, const f32x16& blk, int m0,
-                                            int n0, int lane, int M, int N) {
-  const int m = m0 + (lane & 31);
+// Accumulator layout of one MF x MF block (first MFMA operand from B,
+// second from A): lane l holds row l % MF of the block, and its quad g
+// (elements 4g .. 4g+3) holds the four consecutive columns starting at
+// quad_col(g, l).  32 x 32 blocks: four quads, columns 8g + 4 (l / 32);
+// 16 x 16 blocks: one quad, columns 4 (l / 16).
+template <int MF>
+__device__ __forceinline__ int quad_col(int g, int lane) {
+  return 4 * (g * (64 / MF) + lane / MF);
+}
+
+// Store one accumulator block whose rows start at m0 and columns at n0.
+// Rows >= M and columns >= N are skipped.
+template <typename Cfg, int OUT>
+__device__ __forceinline__ void store_block(void* Cbase, int64_t ld, const typename Cfg::Acc& blk,
+                                            int m0, int n0, int lane, int M, int N) {
+  constexpr int MF = Cfg::kMf;
+  const int m = m0 + lane % MF;
   if (m >= M) return;
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < MF * MF / 256; ++g)
     store_quad<OUT>(Cbase, ld, (f32x4){blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]},
-                    m, n0 + 8 * g + 4 * (lane >> 5), N);
+                    m, n0 + quad_col<MF>(g, lane), N);
 }
 
 // The wave's accumulator blocks into C (bf16 or fp16, or fp32 for the debug
 // output).
 template <typename Cfg, int OUT>
 __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int64_t ld,
-                                           const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                           const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                            int m_base, int n_base, int lane) {
 #pragma unroll
   for (int fm = 0; fm < Cfg::kFragM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < Cfg::kFragN; ++fn)
-      store_block<OUT>(Cbase, ld, acc[fm][fn], m_base + fm * 32, n_base + fn * 32, lane,
-                           a.M, a.N);
+      store_block<Cfg, OUT>(Cbase, ld, acc[fm][fn], m_base + fm * Cfg::kMf,
+                            n_base + fn * Cfg::kMf, lane, a.M, a.N);
 }
 
 // ------------------------------------------------- epilogue through LDS
@@ -584,23 +657,30 @@ __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int
 //
 // Staging layout, per wave: row r of the wave block (kRB bytes) holds
 // 16-byte chunk c at r*kRB + 16 (c ^ sw(r)), sw(r) = r % 16, or (r / 2) % 8
-// for 128-byte rows; 16-bit output further swaps the two 8-byte halves of
-// every chunk in rows with r % 32 >= 16.  With that, the 32 rows one write
-// instruction touches, and the rows one 16-byte read touches, fall in
-// distinct banks.  Blocks too large for the ring go in passes of 32 rows
-// through two alternating buffers.
+// for 128-byte rows.  A write instruction covers MF rows (lanes l and l + MF
+// take the same row), a 16-byte read 64 / (kRB / 16) whole rows; with that
+// XOR both fall in distinct banks, except that with 32 x 32 blocks rows r
+// and r + 16 of one 16-bit write would share them, so there the two 8-byte
+// halves of every chunk are swapped in rows with r % 32 >= 16.  Blocks too
+// large for the ring go in passes of 32 rows through two alternating
+// buffers.
 template <typename Cfg, int OUT>
 struct LdsStage {
+  static constexpr int kMf = Cfg::kMf;
   static constexpr int kE = OUT == kStoreF32 ? 4 : 2;  // bytes per element
   static constexpr int kRB = Cfg::kWaveN * kE;         // bytes per staged row
   static constexpr bool kShape =
       kE == 4 ? (kRB == 256 || kRB == 512) : (kRB == 128 || kRB == 256);
   static constexpr int kWaves = Cfg::kThreads / 64;
   static constexpr bool kWhole = kWaves * Cfg::kWaveM * kRB <= Cfg::kLdsBytes;
-  static constexpr int kFmp = kWhole ? Cfg::kFragM : 1;  // 32-row blocks per pass
-  static constexpr int kBufs = kWhole ? 1 : 2;
-  static constexpr int kWaveBytes = kBufs * kFmp * 32 * kRB;
+  // MFMA block rows per pass: all, or 32 rows
+  static constexpr int kFmp = kWhole || Cfg::kFragM * kMf < 32 ? Cfg::kFragM : 32 / kMf;
+  static constexpr int kPassRows = kFmp * kMf;
+  static constexpr int kBufs = kFmp == Cfg::kFragM ? 1 : 2;
+  static constexpr int kWaveBytes = kBufs * kPassRows * kRB;
+  static constexpr bool kSwapHalves = kE == 2 && kMf == 32;
   static constexpr bool kOk = kShape && kWaves * kWaveBytes <= Cfg::kLdsBytes;
+  static_assert(Cfg::kFragM % kFmp == 0, "whole passes");
 
   __device__ static __forceinline__ uint32_t off(int r, int c) {
     const int sw = kRB == 128 ? (r >> 1) & 7 : r & 15;
@@ -610,46 +690,48 @@ struct LdsStage {
 
 template <typename Cfg, int OUT>
 __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int64_t ld,
-                                               const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                               const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                int m_base, int n_base, int lane) {
   using St = LdsStage<Cfg, OUT>;
   static_assert(St::kOk, "staging fits the ring");
-  constexpr int kE = St::kE, kRB = St::kRB;
+  constexpr int kE = St::kE, kRB = St::kRB, MF = Cfg::kMf;
   constexpr int LPR = kRB / 16;  // lanes per row when reading back
   constexpr int RPI = 64 / LPR;  // rows per read instruction (divides 16)
   static_assert(16 % RPI == 0, "a read instruction's rows share r / 16");
-  const int wr = lane & 31, hi = lane >> 5;
+  static_assert(St::kPassRows % RPI == 0, "whole read instructions per pass");
+  const int wr = lane % MF;
   const int rr = lane / LPR, rc = lane % LPR;
   uint8_t* out = (uint8_t*)Cbase + ((int64_t)(m_base + rr) * ld + n_base) * kE + rc * 16;
 #pragma unroll
   for (int pass = 0; pass < Cfg::kFragM / St::kFmp; ++pass) {
-    lds_u8* buf = region + (pass % St::kBufs) * (St::kFmp * 32 * kRB);
+    lds_u8* buf = region + (pass % St::kBufs) * (St::kPassRows * kRB);
 #pragma unroll
     for (int fi = 0; fi < St::kFmp; ++fi) {
-      const int r = fi * 32 + wr;
+      const int r = fi * MF + wr;
 #pragma unroll
       for (int fn = 0; fn < Cfg::kFragN; ++fn)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& b = acc[pass * St::kFmp + fi][fn];
+        for (int g = 0; g < MF * MF / 256; ++g) {
+          const typename Cfg::Acc& b = acc[pass * St::kFmp + fi][fn];
           const f32x4 v = (f32x4){b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]};
+          const int q4 = (fn * MF + quad_col<MF>(g, lane)) / 4;  // column / 4 in the wave row
           if constexpr (kE == 4) {
-            *(__attribute__((address_space(3))) f32x4*)(buf + St::off(r, fn * 8 + 2 * g + hi)) = v;
+            *(__attribute__((address_space(3))) f32x4*)(buf + St::off(r, q4)) = v;
           } else {
-            const uint32_t h = (uint32_t)((hi ^ (wr >> 4)) & 1);
-            *(__attribute__((address_space(3))) u32x2*)(buf + St::off(r, fn * 4 + g) + (h << 3)) =
+            const uint32_t h = (uint32_t)((q4 ^ (St::kSwapHalves ? wr >> 4 : 0)) & 1);
+            *(__attribute__((address_space(3))) u32x2*)(buf + St::off(r, q4 >> 1) + (h << 3)) =
                 pack_quad<OUT>(v);
           }
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < St::kFmp * 32 / RPI; ++j) {
+    for (int j = 0; j < St::kPassRows / RPI; ++j) {
       const int r = j * RPI + rr;
       u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(buf + St::off(r, rc));
-      if constexpr (kE == 2)
+      if constexpr (St::kSwapHalves)
         if (((j * RPI) & 16) != 0) v = (u32x4){v[2], v[3], v[0], v[1]};
-      *(u32x4*)(out + (int64_t)((pass * St::kFmp * 32 + j * RPI) * kE) * ld) = v;
+      *(u32x4*)(out + (int64_t)((pass * St::kPassRows + j * RPI) * kE) * ld) = v;
     }
   }
 }
@@ -665,7 +747,7 @@ __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int6
 // release fence per workgroup, which writes back that XCD's L2.)
 template <typename Cfg, int OUT, bool SPLIT>
 __device__ __forceinline__ void finish_tile(const KernelArgs& a, lds_u8* smem, int wave, int m0,
-                                            int n0, const f32x16 (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                            int n0, const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                             int m_base, int n_base, int lane, int split) {
   constexpr int kOut = SPLIT ? kStoreF32 : OUT;
   void* const base = SPLIT ? (void*)(a.part + (int64_t)split * a.part_stride) : a.C;

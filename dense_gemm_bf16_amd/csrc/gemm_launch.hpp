@@ -17,7 +17,8 @@ namespace gemm {
 // thread-strided / wave-contiguous dealing of loads;
 // PIPE 6: gemm_bf16_regstage_kernel (loads staged through ST register
 // buffers, two LDS slots);
-// PIPE 8: gemm_bf16_dtl_kernel (LDS-DMA straight into an ST-slot ring);
+// PIPE 8 / 10: gemm_bf16_dtl_kernel (LDS-DMA straight into an ST-slot ring)
+// with 32x32x16 / 16x16x32 MFMAs;
 // PIPE 9: gemm_bf16_wavek_kernel (small M: four waves split each K-step of
 // one BM x 32 block; WM = WN = 1 name the block, 256 threads run it).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int FLAGS>
@@ -29,8 +30,9 @@ hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
   } else if constexpr (PIPE == 6) {
     hipLaunchKernelGGL((gemm_bf16_regstage_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS>),
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
-  } else if constexpr (PIPE == 8) {
-    hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS>),
+  } else if constexpr (PIPE == 8 || PIPE == 10) {
+    hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS,
+                                             PIPE == 10 ? 16 : 32>),
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
   } else if constexpr (PIPE == 9) {
     static_assert(WM == 1 && WN == 1, "one block per workgroup");
@@ -49,6 +51,9 @@ constexpr int lds_bytes_of() {
   return TileCfg<BM, BN, BK, WM, WN, PIPE == 6 ? 2 : ST, SWZ>::kLdsBytes;
 }
 
+// Kernels with a separate K % BK != 0 variant: direct-to-LDS and small M.
+constexpr bool has_partial_variant(int pipe) { return pipe == 8 || pipe == 9 || pipe == 10; }
+
 // The (kOutF32, kSplitK, kRaggedK) combinations that occur, with the fixed
 // bits E (kF16, kPartialK).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
@@ -61,7 +66,7 @@ hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s, int flag
   }
   // K % 8 != 0 (the direct-to-LDS and small-M kernels handle it only in
   // their K % BK != 0 variant, which every such K selects)
-  if constexpr ((PIPE != 8 && PIPE != 9) || (E & kPartialK) != 0) {
+  if constexpr (!has_partial_variant(PIPE) || (E & kPartialK) != 0) {
     switch (flags & 7) {
       case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
       case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 5>(a, grid, s);
@@ -75,7 +80,7 @@ hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s, int flag
 // kernels, kPartialK.
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
 hipError_t launch_partial(const KernelArgs& a, int grid, hipStream_t s, int flags) {
-  if constexpr (PIPE == 8 || PIPE == 9) {
+  if constexpr (has_partial_variant(PIPE)) {
     if (flags & (kPartialK | kRaggedK))
       return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | kPartialK>(a, grid, s, flags);
   }
@@ -126,6 +131,9 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t256x256x64_w2x2_s2_x2_p8, 256, 256, 64, 2, 2, 2, 2, 8, 1, t) \
   X(t256x128x64_w2x2_s3_x2_p8, 256, 128, 64, 2, 2, 3, 2, 8, 1, v) \
   X(t128x128x64_w2x2_s4_x2_p8, 128, 128, 64, 2, 2, 4, 2, 8, 1, w) \
+  X(t256x256x64_w2x2_s2_x3_p10, 256, 256, 64, 2, 2, 2, 3, 10, 1, x) \
+  X(t256x128x64_w2x2_s3_x3_p10, 256, 128, 64, 2, 2, 3, 3, 10, 1, y) \
+  X(t128x128x64_w2x2_s4_x3_p10, 128, 128, 64, 2, 2, 4, 3, 10, 1, z) \
   X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 1, u)     \
   X(t64x32x64_w1x1_s6_x2_p9, 64, 32, 64, 1, 1, 6, 2, 9, 1, u)     \
   X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, 0, j) \

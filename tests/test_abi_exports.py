@@ -90,7 +90,7 @@ def test_argument_checks_need_no_device(lib):
 def test_config_names(lib):
     names = lib.config_names()
     assert len(names) == len(set(names)) >= 2
-    pat = re.compile(r"^t(\d+)x(\d+)x(\d+)_w(\d)x(\d)_s(\d+)_x(\d)_p(\d)$")
+    pat = re.compile(r"^t(\d+)x(\d+)x(\d+)_w(\d)x(\d)_s(\d+)_x(\d)_p(\d+)$")
     for n in names:
         assert pat.match(n), n
     from synthetic_inputs import WORKLOADS

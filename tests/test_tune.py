@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TABLE = os.path.join(ROOT, "dense_gemm_bf16_amd", "csrc", "gemm_tuned.inc")
-PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d)_k(\d+)_g(\d+)(_r\d+)?$")
+PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d+)_k(\d+)_g(\d+)(_r\d+)?$")
 ROW = re.compile(r'^\{(\d+), (\d+), (\d+), "([^"]+)"\},$')
 
 
