@@ -244,15 +244,19 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
 //          16 rows of a phase cover 16 distinct (row-in-256-bytes, chunk)
 //          pairs.  128-byte rows: (row ^ row/8) mod 8; 64-byte rows:
 //          (row / 4) mod 4.
-//   SWZ 3: 128-byte rows: (row ^ (row/8) mod 2) mod 8, the same as SWZ 2
-//          on rows 0..15 but repeating every 16 rows, so just as
-//          conflict-free, and every 16- or 32-row fragment of a wave sees
-//          the same pattern: their read addresses differ by constants only.
+//   SWZ 3: for 16 x 16 x 32 fragments, 128-byte rows: (row / 2) mod 8.
+//          A fragment read takes 16 rows at two adjacent chunks in each
+//          half-wave; counted on MI355X, the LDS serves 32 lanes (512
+//          bytes) at a time, so rows 4 apart must land in different
+//          chunk pairs, which SWZ 2 does not do for this pattern (bank
+//          conflicts doubled the read time).  It repeats every 16 rows, so
+//          all fragments of a wave see one pattern and their read
+//          addresses differ by constants.
 template <int SWZ, int CPR>
 __host__ __device__ constexpr int swz(int row) {
   if constexpr (SWZ == 0) return 0;
   else if constexpr (SWZ == 1) return row & (CPR - 1);
-  else if constexpr (CPR == 8 && SWZ == 3) return (row ^ ((row >> 3) & 1)) & 7;
+  else if constexpr (CPR == 8 && SWZ == 3) return (row >> 1) & 7;
   else if constexpr (CPR == 8) return (row ^ (row >> 3)) & 7;
   else return (row >> 2) & 3;
 }
