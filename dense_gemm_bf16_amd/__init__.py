@@ -23,6 +23,7 @@ GEMM_ERR_INVALID_ARG = 1
 GEMM_ERR_MISALIGNED = 2
 GEMM_ERR_UNSUPPORTED = 3
 GEMM_ERR_HIP = 4
+GEMM_ERR_CAPTURE = 5
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -1,0 +1,4 @@
+// Ablation build only: kernel instantiations of the configurations tagged
+// "w" in GEMM_ABLATION_CONFIGS (gemm_launch.hpp).
+#define GEMM_INST_w GEMM_DO_INST
+#include "gemm_inst_common.hpp"

@@ -26,6 +26,14 @@ int hip_fail(hipError_t e) {
 // One split-K workspace per (device, stream), holding the fp32 partial
 // products of the K-slices.  Work on one stream runs in order, so one buffer
 // per stream is never used by two calls at once.
+//
+// Growth allocates a larger buffer and retires the old one without freeing
+// it: work already queued on the stream, or a graph captured earlier with
+// the old pointer, may still write it.  Retired buffers are freed only by
+// gemm_bf16_release_workspace.  No allocation happens while the stream is
+// being captured (it could not be captured, and the synchronisation that a
+// safe free would need invalidates the capture): the call fails with
+// GEMM_ERR_CAPTURE instead, before anything is enqueued.
 struct Workspace {
   int device;
   hipStream_t stream;
@@ -35,34 +43,39 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
+std::vector<Workspace> g_retired;
+
+// GEMM_OK if the stream is not being captured, else GEMM_ERR_CAPTURE (or
+// GEMM_ERR_HIP if the query fails).
+int check_not_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return hip_fail(e);
+  return st == hipStreamCaptureStatusNone ? GEMM_OK : GEMM_ERR_CAPTURE;
+}
 
 int get_workspace(int device, hipStream_t stream, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  for (Workspace& w : g_ws) {
-    if (w.device != device || w.stream != stream) continue;
-    if (w.bytes >= bytes) {
-      *out = w.ptr;
-      return GEMM_OK;
-    }
-    // grow: the old buffer may still be in use by work queued on `stream`
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e);
-    e = hipFree(w.ptr);
-    if (e != hipSuccess) return hip_fail(e);
-    w.ptr = nullptr;
-    w.bytes = 0;
-    e = hipMalloc(&w.ptr, bytes);
-    if (e != hipSuccess) return hip_fail(e);
-    w.bytes = bytes;
-    *out = w.ptr;
+  Workspace* have = nullptr;
+  for (Workspace& w : g_ws)
+    if (w.device == device && w.stream == stream) have = &w;
+  if (have && have->bytes >= bytes) {
+    *out = have->ptr;
     return GEMM_OK;
   }
-  Workspace w{device, stream, nullptr, 0};
-  hipError_t e = hipMalloc(&w.ptr, bytes);
+  int rc = check_not_capturing(stream);
+  if (rc != GEMM_OK) return rc;
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
   if (e != hipSuccess) return hip_fail(e);
-  w.bytes = bytes;
-  g_ws.push_back(w);
-  *out = w.ptr;
+  if (have) {
+    g_retired.push_back(*have);
+    have->ptr = p;
+    have->bytes = bytes;
+  } else {
+    g_ws.push_back(Workspace{device, stream, p, bytes});
+  }
+  *out = p;
   return GEMM_OK;
 }
 
@@ -324,17 +337,24 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   return GEMM_OK;
 }
 
+// The plan of a call: the named configuration, or the automatic choice.
+int make_plan(const char* config, int64_t M, int64_t N, int64_t K, bool half, Plan* p) {
+  if (config && config[0]) {
+    if (!plan_from_name(config, M, N, K, p)) return GEMM_ERR_UNSUPPORTED;
+  } else {
+    *p = choose_plan(M, N, K, half);
+  }
+  return GEMM_OK;
+}
+
 int gemm_entry(const char* config, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
                void* stream) {
   int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != GEMM_OK) return rc;
   Plan p{};
-  if (config && config[0]) {
-    if (!plan_from_name(config, M, N, K, &p)) return GEMM_ERR_UNSUPPORTED;
-  } else {
-    p = choose_plan(M, N, K, half);
-  }
+  rc = make_plan(config, M, N, K, half, &p);
+  if (rc != GEMM_OK) return rc;
   return run(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32, half, (hipStream_t)stream);
 }
 
@@ -405,6 +425,10 @@ const char* gemm_bf16_status_string(int status) {
       return "unsupported (size beyond 32-bit offsets, unknown config, or a config not built "
              "for fp16)";
     case GEMM_ERR_HIP: return "HIP runtime error (see gemm_bf16_last_hip_error)";
+    case GEMM_ERR_CAPTURE:
+      return "the stream is being captured and this shape needs a larger split-K workspace than "
+             "the one reserved for it (reserve it before capture)";
+
     default: return "unknown status";
   }
 }
@@ -428,18 +452,24 @@ size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
 int gemm_bf16_release_workspace(void) {
   std::lock_guard<std::mutex> lk(gemm::g_ws_mu);
   int rc = GEMM_OK;
-  for (gemm::Workspace& w : gemm::g_ws) {
-    int cur = 0;
-    if (hipGetDevice(&cur) != hipSuccess) cur = w.device;
-    hipError_t e = hipSetDevice(w.device);
-    if (e == hipSuccess) e = hipStreamSynchronize(w.stream);
-    if (e == hipSuccess) e = hipFree(w.ptr);
-    if (e != hipSuccess) rc = gemm::hip_fail(e);
-    // restore the caller's device; a failure here is reported like the rest
-    e = hipSetDevice(cur);
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  auto release = [&](std::vector<gemm::Workspace>& list) {
+    for (gemm::Workspace& w : list) {
+      hipError_t e = hipSetDevice(w.device);
+      if (e == hipSuccess) e = hipStreamSynchronize(w.stream);
+      if (e == hipSuccess) e = hipFree(w.ptr);
+      if (e != hipSuccess) rc = gemm::hip_fail(e);
+    }
+    list.clear();
+  };
+  release(gemm::g_ws);
+  release(gemm::g_retired);
+  // restore the caller's device; a failure here is reported like the rest
+  if (have_cur) {
+    hipError_t e = hipSetDevice(cur);
     if (e != hipSuccess) rc = gemm::hip_fail(e);
   }
-  gemm::g_ws.clear();
   return rc;
 }
 

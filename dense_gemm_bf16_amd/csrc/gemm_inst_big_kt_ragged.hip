@@ -1,0 +1,6 @@
+// Kernel instantiations of the 256 x 256 direct-to-LDS tile ("big" in GEMM_TILE_CONFIGS):
+// bf16 operands, K % 8 != 0.
+#define GEMM_SPLIT_PARAMS GEMM_BIG_PARAMS
+#define GEMM_SPLIT_RAGGED_APART
+#define GEMM_SPLIT_OWN 20
+#include "gemm_inst_split.hpp"

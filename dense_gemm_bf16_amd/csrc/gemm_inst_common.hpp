@@ -1,7 +1,7 @@
-// Body of every gemm_inst_<tu>.hip file: instantiates launch_cfg for the
-// configurations of GEMM_TILE_CONFIGS whose TU tag is this file's.  The
-// including file defines GEMM_INST_<tu> as GEMM_DO_INST before including
-// this header; every other tag expands to nothing.
+// Body of every gemm_inst_<tag>.hip file: instantiates launch_cfg for the
+// rows of GEMM_TILE_CONFIGS (gemm_launch.hpp) whose TU tag is the including
+// file's.  That file defines GEMM_INST_<tag> as GEMM_DO_INST before
+// including this header; every other tag expands to nothing.
 #pragma once
 
 #include "gemm_launch.hpp"
@@ -11,6 +11,21 @@
       const KernelArgs&, int, hipStream_t, int);
 #define GEMM_NO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16)
 
+#ifndef GEMM_INST_big
+#define GEMM_INST_big GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_mid
+#define GEMM_INST_mid GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_mid128
+#define GEMM_INST_mid128 GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_smallm
+#define GEMM_INST_smallm GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_skinny
+#define GEMM_INST_skinny GEMM_NO_INST
+#endif
 #ifndef GEMM_INST_a
 #define GEMM_INST_a GEMM_NO_INST
 #endif
@@ -59,9 +74,6 @@
 #ifndef GEMM_INST_p
 #define GEMM_INST_p GEMM_NO_INST
 #endif
-#ifndef GEMM_INST_q
-#define GEMM_INST_q GEMM_NO_INST
-#endif
 #ifndef GEMM_INST_r
 #define GEMM_INST_r GEMM_NO_INST
 #endif
@@ -71,25 +83,12 @@
 #ifndef GEMM_INST_t
 #define GEMM_INST_t GEMM_NO_INST
 #endif
-#ifndef GEMM_INST_u
-#define GEMM_INST_u GEMM_NO_INST
-#endif
 #ifndef GEMM_INST_v
 #define GEMM_INST_v GEMM_NO_INST
 #endif
 #ifndef GEMM_INST_w
 #define GEMM_INST_w GEMM_NO_INST
 #endif
-#ifndef GEMM_INST_x
-#define GEMM_INST_x GEMM_NO_INST
-#endif
-#ifndef GEMM_INST_y
-#define GEMM_INST_y GEMM_NO_INST
-#endif
-#ifndef GEMM_INST_z
-#define GEMM_INST_z GEMM_NO_INST
-#endif
-
 
 namespace gemm {
 #define GEMM_INSTANTIATE(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU) \

@@ -126,6 +126,7 @@ enum : int {
   kRaggedK = 4,  // K % 8 != 0: patch the 16-byte chunk that straddles K
   kF16 = 8,      // operands (and the 16-bit output) are fp16 instead of bf16
   kPartialK = 16,  // K % BK != 0 (only the direct-to-LDS kernel has a variant for it)
+  kPersistent = 32,  // persistent grid: each workgroup walks several tiles (direct-to-LDS)
 };
 
 // What the epilogue writes.
@@ -666,9 +667,10 @@ __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int
 // XOR both fall in distinct banks, except that with 32 x 32 blocks rows r
 // and r + 16 of one 16-bit write would share them, so there the two 8-byte
 // halves of every chunk are swapped in rows with r % 32 >= 16.  Blocks too
-// large for the ring go in passes of 32 rows through two alternating
-// buffers.
-template <typename Cfg, int OUT>
+// large for the LDS the staging may use (LIMIT bytes: the whole ring, or one
+// slot of it while the other slots receive the next tile's first K-steps)
+// go in passes of 32 rows through two alternating buffers.
+template <typename Cfg, int OUT, int LIMIT = Cfg::kLdsBytes>
 struct LdsStage {
   static constexpr int kMf = Cfg::kMf;
   static constexpr int kE = OUT == kStoreF32 ? 4 : 2;  // bytes per element
@@ -676,14 +678,14 @@ struct LdsStage {
   static constexpr bool kShape =
       kE == 4 ? (kRB == 256 || kRB == 512) : (kRB == 128 || kRB == 256);
   static constexpr int kWaves = Cfg::kThreads / 64;
-  static constexpr bool kWhole = kWaves * Cfg::kWaveM * kRB <= Cfg::kLdsBytes;
+  static constexpr bool kWhole = kWaves * Cfg::kWaveM * kRB <= LIMIT;
   // MFMA block rows per pass: all, or 32 rows
   static constexpr int kFmp = kWhole || Cfg::kFragM * kMf < 32 ? Cfg::kFragM : 32 / kMf;
   static constexpr int kPassRows = kFmp * kMf;
   static constexpr int kBufs = kFmp == Cfg::kFragM ? 1 : 2;
   static constexpr int kWaveBytes = kBufs * kPassRows * kRB;
   static constexpr bool kSwapHalves = kE == 2 && kMf == 32;
-  static constexpr bool kOk = kShape && kWaves * kWaveBytes <= Cfg::kLdsBytes;
+  static constexpr bool kOk = kShape && kWaves * kWaveBytes <= LIMIT;
   static_assert(Cfg::kFragM % kFmp == 0, "whole passes");
 
   __device__ static __forceinline__ uint32_t off(int r, int c) {
@@ -692,11 +694,11 @@ struct LdsStage {
   }
 };
 
-template <typename Cfg, int OUT>
+template <typename Cfg, int OUT, int LIMIT = Cfg::kLdsBytes>
 __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int64_t ld,
                                                const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                int m_base, int n_base, int lane) {
-  using St = LdsStage<Cfg, OUT>;
+  using St = LdsStage<Cfg, OUT, LIMIT>;
   static_assert(St::kOk, "staging fits the ring");
   constexpr int kE = St::kE, kRB = St::kRB, MF = Cfg::kMf;
   constexpr int LPR = kRB / 16;  // lanes per row when reading back
@@ -749,19 +751,21 @@ __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int6
 // (An in-kernel reduction by the last slice to finish a tile was measured
 // 2-3x slower: making the partials visible to the other XCDs needs a
 // release fence per workgroup, which writes back that XCD's L2.)
-template <typename Cfg, int OUT, bool SPLIT>
+template <typename Cfg, int OUT, bool SPLIT, int LIMIT = Cfg::kLdsBytes, bool kBarrier = true>
 __device__ __forceinline__ void finish_tile(const KernelArgs& a, lds_u8* smem, int wave, int m0,
                                             int n0, const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                             int m_base, int n_base, int lane, int split) {
   constexpr int kOut = SPLIT ? kStoreF32 : OUT;
+  using St = LdsStage<Cfg, kOut, LIMIT>;
   void* const base = SPLIT ? (void*)(a.part + (int64_t)split * a.part_stride) : a.C;
   const int64_t ld = SPLIT ? a.ldp : a.ldc;
-  if constexpr (LdsStage<Cfg, kOut>::kOk) {
+  if constexpr (St::kOk) {
     if (m0 + Cfg::kBM <= a.M && n0 + Cfg::kBN <= a.N) {
       // every wave is done with the ring: loads landed, fragments read
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      store_tile_lds<Cfg, kOut>(smem + wave * LdsStage<Cfg, kOut>::kWaveBytes, base, ld, acc,
-                                m_base, n_base, lane);
+      // (kBarrier false: the caller has made sure of it)
+      if constexpr (kBarrier) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      store_tile_lds<Cfg, kOut, LIMIT>(smem + wave * St::kWaveBytes, base, ld, acc, m_base,
+                                       n_base, lane);
       return;
     }
   }

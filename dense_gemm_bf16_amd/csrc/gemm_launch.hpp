@@ -6,9 +6,11 @@
 
 #include "gemm_dtl.hpp"
 #include "gemm_kernel.hpp"
-#include "gemm_pingpong.hpp"
-#include "gemm_regstage.hpp"
 #include "gemm_wavek.hpp"
+#ifdef GEMM_WITH_ABLATION
+#include "ablation/gemm_pingpong.hpp"
+#include "ablation/gemm_regstage.hpp"
+#endif
 
 namespace gemm {
 
@@ -23,6 +25,7 @@ namespace gemm {
 // one BM x 32 block; WM = WN = 1 name the block, 256 threads run it).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int FLAGS>
 hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
+#ifdef GEMM_WITH_ABLATION
   if constexpr (PIPE == 2 || PIPE == 5) {
     static_assert(WM == 2 && WN == 4, "ping-pong runs 2 x 4 waves");
     hipLaunchKernelGGL((gemm_bf16_pingpong_kernel<BM, BN, BK, ST, SWZ, FLAGS, PIPE == 5>),
@@ -30,7 +33,9 @@ hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
   } else if constexpr (PIPE == 6) {
     hipLaunchKernelGGL((gemm_bf16_regstage_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS>),
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
-  } else if constexpr (PIPE == 8 || PIPE == 10) {
+  } else
+#endif
+  if constexpr (PIPE == 8 || PIPE == 10) {
     hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS,
                                              PIPE == 10 ? 16 : 32>),
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
@@ -100,12 +105,41 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   return launch_partial<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 0>(a, grid, s, flags);
 }
 
-// Every built configuration:
+// Built configurations, one row each:
 //   X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ, PIPE, F16, TU)
-// where F16 = 1 also builds it for fp16 operands (the configurations the
-// shape rules pick, and one of each other kernel family), and TU names the
-// gemm_inst_<TU>.hip file that instantiates it.
-#define GEMM_TILE_CONFIGS(X)                                      \
+// where F16 = 1 also builds the row for fp16 operands and TU names the
+// gemm_inst_<TU>.hip file that instantiates it.  A row whose parameters
+// are also needed elsewhere (the files that split its kernel variants over
+// several translation units) takes them from a GEMM_*_PARAMS macro, through
+// GEMM_ROW so the macro expands into separate arguments.
+//
+// The product set is every configuration the shape rules or the tuned
+// table can choose:
+//   big     256 x 256 direct-to-LDS, 16x16x32 MFMAs (4096^3, prefill)
+//   mid     256 x 128 direct-to-LDS, three ring slots (M = 256 decode)
+//   mid128  128 x 128 direct-to-LDS, four ring slots (M = 512 class)
+//   smallm  BM x 32 strips with the waves splitting K (M <= 48)
+//   skinny  32 / 64 x 128 LDS-DMA burst tiles (other M <= 64)
+#define GEMM_ROW(X, ...) X(__VA_ARGS__)
+#define GEMM_BIG_PARAMS 256, 256, 64, 2, 2, 2, 3, 10
+#define GEMM_MID_PARAMS 256, 128, 64, 2, 2, 3, 3, 10
+#define GEMM_PRODUCT_CONFIGS(X)                                        \
+  GEMM_ROW(X, t256x256x64_w2x2_s2_x3_p10, GEMM_BIG_PARAMS, 1, big)     \
+  GEMM_ROW(X, t256x128x64_w2x2_s3_x3_p10, GEMM_MID_PARAMS, 1, mid)     \
+  X(t128x128x64_w2x2_s4_x3_p10, 128, 128, 64, 2, 2, 4, 3, 10, 1, mid128) \
+  X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 1, smallm)     \
+  X(t64x32x64_w1x1_s6_x2_p9, 64, 32, 64, 1, 1, 6, 2, 9, 1, smallm)     \
+  X(t64x128x64_w1x4_s6_x2_p0, 64, 128, 64, 1, 4, 6, 2, 0, 1, skinny)   \
+  X(t32x128x64_w1x4_s6_x2_p0, 32, 128, 64, 1, 4, 6, 2, 0, 1, skinny)
+
+// The ablation set (built only with GEMM_WITH_ABLATION, by
+// build(ablation=True)): the other kernel families and layouts that the
+// measurements behind the product choices compared against -- LDS-DMA
+// spread issue (PIPE 1, 3, 4), ping-pong (2, 5), register-staged (6), the
+// 32x32x16 forms of the direct-to-LDS tiles (8), the unswizzled and
+// row-mod-8 LDS layouts (x0, x1).
+#ifdef GEMM_WITH_ABLATION
+#define GEMM_ABLATION_CONFIGS(X)                                  \
   X(t256x256x64_w2x2_s2_x2_p0, 256, 256, 64, 2, 2, 2, 2, 0, 0, a) \
   X(t256x256x64_w2x2_s2_x2_p3, 256, 256, 64, 2, 2, 2, 2, 3, 0, b) \
   X(t256x256x64_w2x2_s2_x2_p4, 256, 256, 64, 2, 2, 2, 2, 4, 0, c) \
@@ -122,8 +156,6 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t128x128x64_w2x2_s4_x2_p1, 128, 128, 64, 2, 2, 4, 2, 1, 0, i) \
   X(t64x256x64_w1x4_s4_x2_p0, 64, 256, 64, 1, 4, 4, 2, 0, 0, p)   \
   X(t32x256x64_w1x4_s4_x2_p0, 32, 256, 64, 1, 4, 4, 2, 0, 0, p)   \
-  X(t64x128x64_w1x4_s6_x2_p0, 64, 128, 64, 1, 4, 6, 2, 0, 1, q)   \
-  X(t32x128x64_w1x4_s6_x2_p0, 32, 128, 64, 1, 4, 6, 2, 0, 1, q)   \
   X(t64x256x64_w1x4_s4_x2_p6, 64, 256, 64, 1, 4, 4, 2, 6, 0, r)   \
   X(t32x256x64_w1x4_s4_x2_p6, 32, 256, 64, 1, 4, 4, 2, 6, 0, r)   \
   X(t256x128x64_w2x2_s2_x2_p6, 256, 128, 64, 2, 2, 2, 2, 6, 1, s) \
@@ -131,13 +163,13 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t256x256x64_w2x2_s2_x2_p8, 256, 256, 64, 2, 2, 2, 2, 8, 1, t) \
   X(t256x128x64_w2x2_s3_x2_p8, 256, 128, 64, 2, 2, 3, 2, 8, 1, v) \
   X(t128x128x64_w2x2_s4_x2_p8, 128, 128, 64, 2, 2, 4, 2, 8, 1, w) \
-  X(t256x256x64_w2x2_s2_x3_p10, 256, 256, 64, 2, 2, 2, 3, 10, 1, x) \
-  X(t256x128x64_w2x2_s3_x3_p10, 256, 128, 64, 2, 2, 3, 3, 10, 1, y) \
-  X(t128x128x64_w2x2_s4_x3_p10, 128, 128, 64, 2, 2, 4, 3, 10, 1, z) \
-  X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 1, u)     \
-  X(t64x32x64_w1x1_s6_x2_p9, 64, 32, 64, 1, 1, 6, 2, 9, 1, u)     \
   X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, 0, j) \
   X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, 0, j)
+#else
+#define GEMM_ABLATION_CONFIGS(X)
+#endif
+
+#define GEMM_TILE_CONFIGS(X) GEMM_PRODUCT_CONFIGS(X) GEMM_ABLATION_CONFIGS(X)
 
 #define GEMM_DECLARE_LAUNCH(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU) \
   extern template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16>(  \

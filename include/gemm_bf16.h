@@ -38,13 +38,18 @@
  * retains them.  C must not overlap A or B.  When a shape's configuration
  * splits K, the fp32 partial sums of the S slices (S * M * roundup8(N) * 4
  * bytes) go to a workspace the library owns per (device, stream): allocated
- * on first need, grown when a larger one is needed (growth synchronises that
- * stream), freed by gemm_bf16_release_workspace.  Pre-size it with gemm_bf16_reserve_workspace
- * before stream capture, since allocation cannot be captured.
+ * on first need and grown when a larger one is needed.  Growth allocates a
+ * new buffer and keeps the old one alive (work already queued, or a graph
+ * captured earlier, may still use it); all of them are freed by
+ * gemm_bf16_release_workspace, which therefore invalidates graphs captured
+ * with calls that split K.  Allocation cannot be captured: pre-size the
+ * workspace with gemm_bf16_reserve_workspace before stream capture; a call
+ * under capture that would need to grow it returns GEMM_ERR_CAPTURE without
+ * enqueueing anything.
  *
  * Streams and errors.  Calls are asynchronous: work is enqueued on `stream`
  * (a hipStream_t passed as void*, NULL = the null stream) and the call never
- * synchronises it, except when growing a workspace.  Argument errors are
+ * synchronises it.  Argument errors are
  * returned synchronously before anything is enqueued.  A device fault shows
  * up at the caller's next synchronisation.  Calls on different streams may
  * run concurrently.  Nothing aborts and nothing prints.
@@ -68,6 +73,9 @@ extern "C" {
                                   built for fp16 passed to gemm_f16_ex */
 #define GEMM_ERR_HIP 4         /* a HIP runtime call failed; see
                                   gemm_bf16_last_hip_error */
+#define GEMM_ERR_CAPTURE 5     /* the stream is being captured and the call
+                                  would have to allocate a larger split-K
+                                  workspace (reserve it before capture) */
 
 /* C = A * B^T with bf16 output.  Arguments as described above.  Returns a
  * status code. */

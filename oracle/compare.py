@@ -17,6 +17,10 @@ tolerance; the readings below are stated in the design notes):
   held to the same rule in fp16 ulps (both formats are sign-magnitude, so
   adjacent values of either differ by one in the ordering key below).
 * fp32 debug output: |C32 - s| <= 1e-4 * sqrt(K) * sigma_A * sigma_B.
+
+The floor relaxes "within 1 ulp" for the elements near zero only; reports
+carry ``max_ulp`` and ``n_floor`` (elements beyond 1 ulp that passed by the
+floor), so how many needed it is always visible.
 """
 from __future__ import annotations
 

@@ -45,13 +45,31 @@ def test_measured_traffic_only_for_matching_sources_and_config(tmp_path, monkeyp
     h = bench.kernel_source_hash()
     expect = hashlib.sha256(b"k.hip" + b"kernel v1\n").hexdigest()[:16]
     assert h == expect
-    rec = {"w": {"kernel_src_hash": h, "config": "cfg_a", "hbm_bytes_per_launch": 1234}}
+    rec = {"w": {"kernel_src_hash": h, "config": "cfg_a", "l2_fabric_bytes_per_launch": 1234}}
     _write_traffic(str(tmp_path), rec)
     assert bench.measured_traffic("w", "cfg_a") == 1234
     assert bench.measured_traffic("w", "cfg_b") is None        # another plan
     assert bench.measured_traffic("other", "cfg_a") is None    # another workload
     (src / "k.hip").write_text("kernel v2\n")                  # the kernel changed
     assert bench.measured_traffic("w", "cfg_a") is None
+    (src / "k.hip").write_text("kernel v1\n")
+    (src / "sub").mkdir()                                      # files in subfolders count
+    (src / "sub" / "a.hpp").write_text("x\n")
+    assert bench.kernel_source_hash() != h
+
+
+def test_cpu_model_reads_the_host():
+    info = bench.cpu_model()
+    assert info["logical_cpus"] == os.cpu_count()
+    assert info["model"] is None or isinstance(info["model"], str)
+
+
+def test_clock_summary():
+    s = [{"gfx": [1800, 1900], "mem": 1300}, None, {"gfx": [2000], "mem": 1300}]
+    c = bench.summarize_clocks(s)
+    assert c["sclk_mhz_median"] == 1900 and c["sclk_mhz_min"] == 1800
+    assert c["sclk_mhz_max"] == 2000 and c["mclk_mhz_median"] == 1300
+    assert bench.summarize_clocks([None]) is None
 
 
 def test_committed_traffic_record_adds_up():
@@ -62,5 +80,5 @@ def test_committed_traffic_record_adds_up():
     for name, rec in table.items():
         want = (rec["fetch_kib_per_launch"] * 1024 * rec["copy_fetch_factor"]
                 + rec["write_kib_per_launch"] * 1024 * rec["copy_write_factor"])
-        assert rec["hbm_bytes_per_launch"] == pytest.approx(want, rel=2e-4), name
+        assert rec["l2_fabric_bytes_per_launch"] == pytest.approx(want, rel=2e-4), name
         assert os.path.exists(os.path.join(ROOT, rec["source"])), name

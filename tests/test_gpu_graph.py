@@ -49,3 +49,36 @@ def test_graph_replays_match_oracle(shape):
         bad = int(np.count_nonzero(got != ref16))
         print(shape, "replay", rep, "mismatches", bad, flush=True)
         assert bad == 0, (shape, rep, bad)
+
+
+def test_capture_that_needs_a_larger_workspace_is_refused():
+    """A call captured on a stream whose workspace is too small returns
+    GEMM_ERR_CAPTURE without allocating, synchronising or enqueueing, so the
+    capture itself stays valid; the same call made eagerly afterwards
+    allocates and is exact."""
+    import torch
+
+    import dense_gemm_bf16_amd as g
+    import oracle
+
+    # larger partials than the other tests reserve on any stream (torch hands
+    # out its streams from a pool, so this stream may have been used before)
+    M, N, K = 256, 12800, 4608
+    assert g.workspace_size(M, N, K) > 32 << 20
+    A = int_bf16(M, K, seed=850)
+    B = int_bf16(N, K, seed=851)
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    dC = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    s = torch.cuda.Stream()  # a new stream: no workspace reserved for it
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        rc = g.gemm_bf16_status(M, N, K, dA, K, dB, K, dC, N, stream=s.cuda_stream)
+    print("status under capture", rc, g.status_string(rc), flush=True)
+    assert rc == g.GEMM_ERR_CAPTURE
+    with torch.cuda.stream(s):
+        g.gemm_bf16(M, N, K, dA, K, dB, K, dC, N, stream=s)
+    torch.cuda.synchronize()
+    ref16, _ = oracle.gemm(A, B)
+    assert np.array_equal(dC.cpu().numpy().view(np.uint16), ref16)

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from oracle.compare import check_bf16, check_f32
-from synthetic_inputs import WORKLOADS, int_bf16, normal_bf16
+from synthetic_inputs import WORKLOADS, f32_to_bf16_bits, int_bf16, normal_bf16
 from tests.gpu_util import run_gemm
 
 pytestmark = pytest.mark.gpu
@@ -29,16 +29,26 @@ def _oracle():
 
 
 def _full_check(w, A, B, exact):
+    """bf16 output against the oracle's rounded sums, the fp32 debug output
+    against its exact sums, and the debug output rounded to bf16 against the
+    bf16 output: the two calls share plan and summation order, so they must
+    agree bit for bit (this also holds on plans that split K, where the fp32
+    result comes out of the reduction kernel's fp32 branch)."""
     o = _oracle()
     ref16, ref64 = o.gemm(A, B, K=w.K)
     got = run_gemm(A, B, K=w.K)
+    import dense_gemm_bf16_amd as g
+
+    plan = g.config_name(w.M, w.N, w.K)
     rep = check_bf16(got, ref16, ref64, w.K, w.sigma_a, w.sigma_b, exact=exact)
-    print(w.name, "bf16", rep, flush=True)
+    print(w.name, plan, "bf16", rep, flush=True)
     assert rep["ok"], rep
     got32 = run_gemm(A, B, K=w.K, out_f32=True)
     rep32 = check_f32(got32, ref64, w.K, w.sigma_a, w.sigma_b, exact=exact)
-    print(w.name, "f32", rep32, flush=True)
+    print(w.name, plan, "f32", rep32, flush=True)
     assert rep32["ok"], rep32
+    rounded = f32_to_bf16_bits(got32)
+    assert np.array_equal(rounded, got), (w.name, int(np.count_nonzero(rounded != got)))
 
 
 @pytest.mark.parametrize("name", ["square512_int", "square512_normal"])
@@ -58,27 +68,21 @@ def test_square4096_full(name):
 @pytest.mark.parametrize("name", ["decode_attn_out", "decode_qkv", "decode_mlp_up",
                                   "decode_mlp_down"])
 def test_decode_full(name):
+    """Every element, bf16 and fp32 output; attention-out, QKV and MLP-down
+    split K, so their fp32 output comes from the reduction kernel."""
     w = WORKLOADS[name]
     A, B = w.make()
-    o = _oracle()
-    ref16, ref64 = o.gemm(A, B, K=w.K)
-    got = run_gemm(A, B)
-    rep = check_bf16(got, ref16, ref64, w.K, w.sigma_a, w.sigma_b)
-    print(name, rep, flush=True)
-    assert rep["ok"], rep
+    _full_check(w, A, B, exact=False)
 
 
 @pytest.mark.parametrize("name", ["proj_512x8192x5376", "ragged_m1", "ragged_m17",
                                   "ragged_m64", "ragged_m200"])
 def test_irregular_full(name):
+    """Every element, bf16 and fp32 output: M = 1 and 17 run the small-M
+    kernel (its own fp32 store), M = 64 and 200 split K."""
     w = WORKLOADS[name]
     A, B = w.make()
-    o = _oracle()
-    ref16, ref64 = o.gemm(A, B, K=w.K)
-    got = run_gemm(A, B)
-    rep = check_bf16(got, ref16, ref64, w.K, w.sigma_a, w.sigma_b)
-    print(name, rep, flush=True)
-    assert rep["ok"], rep
+    _full_check(w, A, B, exact=False)
 
 
 @pytest.mark.parametrize("name", ["prefill_attn_out", "prefill_mlp_up"])
@@ -125,6 +129,13 @@ def test_every_config_bit_exact_on_ragged_shape():
             rep = check_bf16(got, ref16, None, K, exact=True)
             print(name, rep, flush=True)
             assert rep["ok"], (name, rep)
+        # fp32 debug output: the kernel's own fp32 store and the reduction's
+        for suffix in ("_k1", "_k3"):
+            name = cfg + suffix
+            got32 = run_gemm(A, B, config=name, out_f32=True)
+            rep = check_f32(got32, ref64, K, exact=True)
+            print(name, "f32", rep, flush=True)
+            assert rep["ok"], (name, rep)
 
 
 def test_every_config_bit_exact_with_k_not_multiple_of_8():
@@ -139,13 +150,17 @@ def test_every_config_bit_exact_with_k_not_multiple_of_8():
     B = np.full((N, ld), 0x7FC0, np.uint16)
     A[:, :K] = int_bf16(M, K, seed=103)
     B[:, :K] = int_bf16(N, K, seed=104)
-    ref16, _ = _oracle().gemm(A, B, K=K)
+    ref16, ref64 = _oracle().gemm(A, B, K=K)
     for cfg in g.config_names():
         for suffix in ("_k1", "_k2_g4_r1"):
             name = cfg + suffix
             got = run_gemm(A, B, K=K, config=name)
             rep = check_bf16(got, ref16, None, K, exact=True)
             print(name, rep, flush=True)
+            assert rep["ok"], (name, rep)
+            got32 = run_gemm(A, B, K=K, config=name, out_f32=True)
+            rep = check_f32(got32, ref64, K, exact=True)
+            print(name, "f32", rep, flush=True)
             assert rep["ok"], (name, rep)
 
 
@@ -212,18 +227,22 @@ def test_empty_m_or_n_is_noop():
 
 def test_split_k_matches_unsplit_on_integers():
     """Decode shape with integer inputs: split and unsplit both bit-exact,
-    for every slice count the reduction has a fixed-count kernel for (2-8)
-    and for one beyond (16, the run-time count loop)."""
+    bf16 output and fp32 output (which equals the exact sum: every partial
+    and every fixed-order slice sum is an integer below 2^24), for slice
+    counts 1-8 and 16."""
     M, N, K = 256, 1024, 8192
     A = int_bf16(M, K, seed=600)
     B = int_bf16(N, K, seed=601)
     import dense_gemm_bf16_amd as g
 
-    ref16, _ = _oracle().gemm(A, B)
+    ref16, ref64 = _oracle().gemm(A, B)
     tile = g.config_name(M, N, K).split("_k")[0]
     for cfg in [f"{tile}_k{k}" for k in (1, 2, 3, 4, 5, 6, 7, 8, 16)]:
         got = run_gemm(A, B, config=cfg)
         assert check_bf16(got, ref16, None, K, exact=True)["ok"], cfg
+        got32 = run_gemm(A, B, config=cfg, out_f32=True)
+        rep = check_f32(got32, ref64, K, exact=True)
+        assert rep["ok"], (cfg, rep)
 
 
 def test_deterministic_repeat():
@@ -272,3 +291,35 @@ def test_random_shapes_automatic_plan_bit_exact():
         print(i, (M, N, K), plan, rep, flush=True)
         assert rep["ok"], ((M, N, K), plan, rep)
     print("tiles used:", sorted(plans), flush=True)
+
+
+PRODUCT_CONFIGS = {
+    "t256x256x64_w2x2_s2_x3_p10", "t256x128x64_w2x2_s3_x3_p10", "t128x128x64_w2x2_s4_x3_p10",
+    "t32x32x64_w1x1_s8_x2_p9", "t64x32x64_w1x1_s6_x2_p9", "t64x128x64_w1x4_s6_x2_p0",
+    "t32x128x64_w1x4_s6_x2_p0",
+}
+
+
+def test_ablation_configurations_when_built():
+    """The configurations of csrc/ablation (the kernel families and LDS
+    layouts the product choices were measured against) exist only in
+    build(ablation=True); there they must be as exact as the product ones,
+    plain and split, bf16 and fp32 output."""
+    import dense_gemm_bf16_amd as g
+
+    names = set(g.config_names())
+    assert PRODUCT_CONFIGS <= names, sorted(PRODUCT_CONFIGS - names)
+    extra = sorted(names - PRODUCT_CONFIGS)
+    if not extra:
+        pytest.skip("ablation build absent: the default build holds only the product "
+                    "configurations; build(ablation=True) adds csrc/ablation's")
+    M, N, K = 300, 520, 456
+    A = int_bf16(M, K, seed=105)
+    B = int_bf16(N, K, seed=106)
+    ref16, ref64 = _oracle().gemm(A, B)
+    for cfg in extra:
+        for suffix in ("_k1", "_k3"):
+            got = run_gemm(A, B, config=cfg + suffix)
+            assert check_bf16(got, ref16, None, K, exact=True)["ok"], cfg + suffix
+            got32 = run_gemm(A, B, config=cfg + suffix, out_f32=True)
+            assert check_f32(got32, ref64, K, exact=True)["ok"], cfg + suffix

@@ -52,9 +52,12 @@ def test_square_f16(name):
 @pytest.mark.parametrize("name", ["decode_attn_out", "decode_mlp_down", "proj_512x8192x5376",
                                   "ragged_m1", "ragged_m17", "ragged_m64", "ragged_m200"])
 def test_decode_and_irregular_f16(name):
+    """fp16 and fp32 output on every element: split-K plans (attention-out,
+    MLP-down, M = 64 and 200) take the reduction's fp32 branch, M = 1 and
+    17 the small-M kernel's fp32 store."""
     w = WORKLOADS[name]
     A, B = w.make(fmt=F16)
-    _check_full(w, A, B, exact=False, f32=False)
+    _check_full(w, A, B, exact=False, f32=True)
 
 
 def test_prefill_sampled_f16():
@@ -90,13 +93,19 @@ def test_every_f16_config_bit_exact_on_ragged_shape():
     ref16, ref64 = _oracle().gemm(A, B, fmt=F16)
     assert (np.abs(ref64) > 2048).mean() > 0.1
     names = g.f16_config_names()
-    assert "t256x256x64_w2x2_s2_x2_p6" in names
+    assert "t256x256x64_w2x2_s2_x3_p10" in names
     for cfg in names:
         for suffix in ("_k1", "_k3", "_k2_g4_r1"):
             name = cfg + suffix
             got = run_gemm(A, B, config=name, fmt=F16)
             rep = check_bf16(got, ref16, None, K, exact=True, fmt=F16)
             print(name, rep, flush=True)
+            assert rep["ok"], (name, rep)
+        for suffix in ("_k1", "_k3"):
+            name = cfg + suffix
+            got32 = run_gemm(A, B, config=name, out_f32=True, fmt=F16)
+            rep = check_f32(got32, ref64, K, exact=True)
+            print(name, "f32", rep, flush=True)
             assert rep["ok"], (name, rep)
 
 
@@ -115,7 +124,7 @@ def test_ragged_k_f16(K):
     assert check_f32(got32, ref64, K, exact=True)["ok"]
 
 
-@pytest.mark.parametrize("config", [None, "t256x128x64_w2x2_s2_x2_p6_k3",
+@pytest.mark.parametrize("config", [None, "t256x128x64_w2x2_s3_x3_p10_k3",
                                     "t32x128x64_w1x4_s6_x2_p0_k1"])
 def test_overflow_threshold_f16(config):
     """Sums 65504 (largest finite), 65519 (rounds down to it), 65520 (the
