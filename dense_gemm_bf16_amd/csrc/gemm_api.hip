@@ -156,10 +156,19 @@ int choose_splits(int64_t tiles, int64_t k_tiles, int64_t target = kCUs) {
 }
 
 void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
   const int64_t bk = p->tile->bk;
   const int64_t k_tiles = (K + bk - 1) / bk;
+  if (p->persist > 0) {
+    // a persistent grid walks whole tiles (no split); it is a multiple of 8
+    // workgroups, so each keeps its XCD's tiles, and no larger than the
+    // tile count
+    p->splits = 1;
+    const int64_t tiles = ((M + p->tile->bm - 1) / p->tile->bm) * ((N + p->tile->bn - 1) / p->tile->bn);
+    int64_t g = p->persist / 8 * 8;
+    if (g < 8) g = 8;
+    if (g > tiles) g = tiles;
+    p->persist = (int)(g > 0 ? g : 8);
+  }
   if (p->splits > k_tiles) p->splits = (int)(k_tiles > 0 ? k_tiles : 1);
   if (p->splits < 1) p->splits = 1;
   if (p->splits > 1) {
@@ -167,10 +176,11 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
     const int64_t per = (k_tiles + p->splits - 1) / p->splits;
     p->splits = (int)((k_tiles + per - 1) / per);
   }
-  const int n = snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
+  int n = snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
   if (p->k_rot > 0 && n > 0 && n < (int)sizeof p->name)
-    snprintf(p->name + n, sizeof p->name - n, "_r%d", p->k_rot);
-
+    n += snprintf(p->name + n, sizeof p->name - n, "_r%d", p->k_rot);
+  if (p->persist > 0 && n > 0 && n < (int)sizeof p->name)
+    snprintf(p->name + n, sizeof p->name - n, "_P%d", p->persist);
 }
 
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out);
@@ -224,13 +234,14 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
   return p;
 }
 
-// Parse "tile[_k<splits>][_g<group>][_r<rotation>]" where tile is a table
-// name.
+// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>]" where tile is a
+// table name (_P: a persistent grid of that many workgroups walking the
+// tiles; only for tiles built with it, bf16 operands, and never split).
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out) {
   char buf[64];
   if (strlen(name) >= sizeof buf) return false;
   strcpy(buf, name);
-  int splits = 1, group = 4, rot = 0;
+  int splits = 1, group = 4, rot = 0, persist = 0;
   for (;;) {
     char* u = strrchr(buf, '_');
     if (!u) break;
@@ -244,6 +255,9 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
     } else if (u[1] == 'r' && sscanf(u + 2, "%d", &v) == 1 && v >= 0) {
       rot = v;
       *u = 0;
+    } else if (u[1] == 'P' && sscanf(u + 2, "%d", &v) == 1 && v >= 1) {
+      persist = v;
+      *u = 0;
 
     } else {
       break;
@@ -251,10 +265,12 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
   }
   const TileConfig* t = find_tile_config(buf);
   if (!t) return false;
+  if (persist > 0 && (!t->persist || splits > 1)) return false;
   out->tile = t;
   out->splits = splits;
   out->group_m = group;
   out->k_rot = rot;
+  out->persist = persist;
   finish_plan(out, M, N, K);
   return true;
 }
@@ -278,6 +294,7 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
         hipStream_t stream) {
   const TileConfig& t = *p.tile;
   if (half && !t.f16) return GEMM_ERR_UNSUPPORTED;
+  if (p.persist > 0 && (half || !t.persist || p.splits > 1)) return GEMM_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return GEMM_OK;
   // 32-bit limits: tile-relative byte offsets of the operands, grid size,
   // and the int32 shape fields of the kernel.
@@ -290,8 +307,9 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
     return GEMM_ERR_UNSUPPORTED;
   const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
   const int64_t k_tiles = (K + t.bk - 1) / t.bk;
-  const int64_t grid = tiles_m * tiles_n * p.splits;
-  if (grid >= (int64_t(1) << 31)) return GEMM_ERR_UNSUPPORTED;
+  const int64_t units = tiles_m * tiles_n * p.splits;
+  if (units >= (int64_t(1) << 31)) return GEMM_ERR_UNSUPPORTED;
+  const int64_t grid = p.persist > 0 && !out_f32 && p.persist < units ? p.persist : units;
 
   KernelArgs a{};
   a.A = (const uint16_t*)A;
@@ -314,6 +332,8 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   if ((K & 7) != 0) flags |= kRaggedK;
   if (half) flags |= kF16;
   if (K % t.bk != 0) flags |= kPartialK;
+  // (fp32 output: the ordinary kernel, whose per-tile K order is the same)
+  if (p.persist > 0 && !out_f32) flags |= kPersistent;
   void* ws = nullptr;
   if (p.splits > 1) {
     int dev = 0;

@@ -7,12 +7,13 @@
 namespace gemm {
 
 const TileConfig* tile_configs() {
-#define GEMM_TABLE_ROW(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU)                 \
+#define GEMM_TABLE_ROW(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT, TU)                 \
   {#NAME, BM, BN, BK, PIPE == 9 ? 256 : WM * WN * 64,                                  \
    lds_bytes_of<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(),                                     \
-   F16 != 0, &launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16>},
+   (OPT & kOptF16) != 0, (OPT & kOptPersist) != 0,                                        \
+   &launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT>},
   static const TileConfig table[] = {
-      GEMM_TILE_CONFIGS(GEMM_TABLE_ROW){nullptr, 0, 0, 0, 0, 0, false, nullptr}};
+      GEMM_TILE_CONFIGS(GEMM_TABLE_ROW){nullptr, 0, 0, 0, 0, 0, false, false, nullptr}};
 #undef GEMM_TABLE_ROW
   return table;
 }

@@ -86,31 +86,16 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- which tile and which K-slice (as in the other kernels) -------------
+  // A work unit is one (tile, K-slice).  Each workgroup takes unit
+  // blockIdx.x, and with a persistent grid also blockIdx.x + gridDim.x,
+  // + 2 gridDim.x, ...: unit v runs on XCD v % 8 either way (the grid is a
+  // multiple of 8), so xcd_remap gives the same tile order per XCD as a grid
+  // of one workgroup per unit.
+  constexpr bool kPersist = (FLAGS & kPersistent) != 0;
+  static_assert(!(kPersist && kSplit), "a persistent grid does not split K");
   const int ntiles = a.tiles_m * a.tiles_n;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = kSplit ? logical / ntiles : 0;
-  const int t = logical - split * ntiles;
-  int tm, tn;
-  {
-    const int span = a.group_m * a.tiles_n;
-    const int gid = t / span;
-    const int first_m = gid * a.group_m;
-    const int gsz = min(a.tiles_m - first_m, a.group_m);
-    const int in = t - gid * span;
-    tm = first_m + in % gsz;
-    tn = in / gsz;
-  }
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kt_begin = split * a.k_tiles_per_split;
-  const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
-  const int n_iter = kt_end - kt_begin;
-  const KOrder korder = make_korder(a, t, kt_begin, n_iter);
+  const int units = kSplit ? ntiles * a.splits : ntiles;
   const int full_tiles = a.K / BK;  // K-steps wholly inside K
-
-  const int rows_a = min(BM, a.M - m0);
-  const int rows_b = min(BN, a.N - n0);
-  const u32x4 rsrc_a = make_rsrc(a.A + (int64_t)m0 * a.lda, (uint32_t)(rows_a * a.lda * 2));
-  const u32x4 rsrc_b = make_rsrc(a.B + (int64_t)n0 * a.ldb, (uint32_t)(rows_b * a.ldb * 2));
 
   // Per-lane offsets of this thread's loads (see the header comment).
   constexpr int RPI = T / CPR;  // rows covered by one load of all threads
@@ -121,16 +106,50 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   int chunk2[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) chunk2[p] = c0 ^ swz<SWZ, CPR>(p * RPI + r0);
+
+  // The current unit's tile, K range and load addressing.
+  int split = 0, m0 = 0, n0 = 0, n_iter = 0;
+  KOrder korder{0, 0, 0};
+  u32x4 rsrc_a, rsrc_b;
   uint32_t voff[L];
+  auto setup = [&](int unit) __attribute__((always_inline)) {
+    const int logical = xcd_remap(unit, units);
+    split = kSplit ? logical / ntiles : 0;
+    const int t = logical - split * ntiles;
+    const int span = a.group_m * a.tiles_n;
+    const int gid = t / span;
+    const int first_m = gid * a.group_m;
+    const int gsz = min(a.tiles_m - first_m, a.group_m);
+    const int in = t - gid * span;
+    m0 = (first_m + in % gsz) * BM;
+    n0 = (in / gsz) * BN;
+    const int kt_begin = split * a.k_tiles_per_split;
+    const int kt_end = kSplit ? min(a.k_tiles, kt_begin + a.k_tiles_per_split) : a.k_tiles;
+    n_iter = kt_end - kt_begin;
+    korder = make_korder(a, t, kt_begin, n_iter);
+    const int rows_a = min(BM, a.M - m0);
+    const int rows_b = min(BN, a.N - n0);
+    rsrc_a = make_rsrc(a.A + (int64_t)m0 * a.lda, (uint32_t)(rows_a * a.lda * 2));
+    rsrc_b = make_rsrc(a.B + (int64_t)n0 * a.ldb, (uint32_t)(rows_b * a.ldb * 2));
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const bool is_a = i < LA;
-    const int ii = is_a ? i : i - LA;
-    const int row = ii * RPI + r0;
-    const int ld = (int)(is_a ? a.lda : a.ldb);
-    voff[i] = row < (is_a ? rows_a : rows_b) ? (uint32_t)(row * ld * 2 + chunk2[ii & 1] * 16)
-                                             : kOOB;
-  }
+    for (int i = 0; i < L; ++i) {
+      const bool is_a = i < LA;
+      const int ii = is_a ? i : i - LA;
+      const int row = ii * RPI + r0;
+      const int ld = (int)(is_a ? a.lda : a.ldb);
+      voff[i] = row < (is_a ? rows_a : rows_b) ? (uint32_t)(row * ld * 2 + chunk2[ii & 1] * 16)
+                                               : kOOB;
+    }
+  };
+  int unit = blockIdx.x;
+  setup(unit);
+
+  // Byte offset of the ring slot of K-step Y.  With a persistent grid, step
+  // 0 of every unit goes to slot 1: slot 0 then stages the previous unit's C
+  // while the next unit's first S-1 steps land in slots 1 .. S-1.
+  auto slot_off = [](int Y) __attribute__((always_inline)) {
+    return (uint32_t)(((kPersist ? Y + 1 : Y) % S) * Cfg::kStageBytes);
+  };
 
   // LDS byte offset (within a slot) of load i's 1 KB of this wave.
   auto lds_off = [&](int i) __attribute__((always_inline)) {
@@ -140,7 +159,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   // Load i of step Y (Y < n_iter).
   auto dma_one = [&](int Y, int i) __attribute__((always_inline)) {
     const int kt = korder.kt(Y);
-    const uint32_t dst = smem_addr + (uint32_t)((Y % S) * Cfg::kStageBytes) + lds_off(i);
+    const uint32_t dst = smem_addr + slot_off(Y) + lds_off(i);
     const u32x4& rs = i < LA ? rsrc_a : rsrc_b;
     if constexpr (kPartial) {
       if (kt >= full_tiles) {
@@ -158,7 +177,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   // (after its loads have landed).
   auto trim_tail = [&](int Y) __attribute__((always_inline)) {
     const int k0 = korder.kt(Y) * BK;
-    lds_u8* slot = smem + (Y % S) * Cfg::kStageBytes;
+    lds_u8* slot = smem + slot_off(Y);
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int ii = i < LA ? i : i - LA;
@@ -189,13 +208,16 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   };
 
   typename Cfg::Acc acc[Cfg::kFragM][Cfg::kFragN];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < Cfg::kFragM; ++i)
+    for (int i = 0; i < Cfg::kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::kFragN; ++j)
+      for (int j = 0; j < Cfg::kFragN; ++j)
 #pragma unroll
-      for (int r = 0; r < MF * MF / 64; ++r) acc[i][j][r] = 0.0f;
-  if constexpr (MF == 16) mfma16_settle();
+        for (int r = 0; r < MF * MF / 64; ++r) acc[i][j][r] = 0.0f;
+    if constexpr (MF == 16) mfma16_settle();
+  };
+  zero_acc();
   // B fragments alternate between two buffers per substep.  A fragments
   // too with 32 x 32 blocks; with 16 x 16 blocks (twice as many fragments)
   // there is one A buffer, and fragment fm of the next substep replaces
@@ -203,33 +225,46 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   constexpr int kABufs = MF == 16 ? 1 : 2;
   bf16x8 fa[kABufs][Cfg::kFragM], fb[2][Cfg::kFragN];
 
-  // ---- prologue: steps 0..S-2 whole, group 0 of step S-1 -------------------
+  // ---- prologue: steps 0..S-2 whole (head), group 0 of step S-1 (tail),
+  // then wait for step 0 and read its first fragments --------------------
   constexpr int G = L / F;
+  auto prologue_head = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int p = 0; p + 1 < S; ++p)
-    if (p < n_iter)
+    for (int p = 0; p + 1 < S; ++p)
+      if (p < n_iter)
 #pragma unroll
-      for (int i = 0; i < L; ++i) dma_one(p, i);
-  const bool g0 = S - 1 < n_iter;
-  if (g0)
+        for (int i = 0; i < L; ++i) dma_one(p, i);
+  };
+  auto prologue_tail = [&]() __attribute__((always_inline)) {
+    if (S - 1 < n_iter)
 #pragma unroll
-    for (int i = 0; i < G; ++i) dma_one(S - 1, i);
-  if (n_iter > 0) {
-    if constexpr (kRagged) {
-      if (korder.kt(0) == a.k_tiles - 1) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        trim_tail(0);
+      for (int i = 0; i < G; ++i) dma_one(S - 1, i);
+  };
+  // In flight after step 0: steps 1 .. min(S-2, n_iter-1) whole and group 0
+  // of step S-1 if it exists.  (With a persistent grid the previous unit's C
+  // stores were issued between head and tail; loads land in order, so the
+  // count below still proves that step 0 has landed.)
+  auto prologue_wait = [&]() __attribute__((always_inline)) {
+    if (n_iter > 0) {
+      if constexpr (kRagged) {
+        if (korder.kt(0) == a.k_tiles - 1) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          trim_tail(0);
+        }
       }
+      ring_wait_barrier_ng<L, S - 2, G>(min(S - 2, n_iter - 1), S - 1 < n_iter);
+      const lds_u8* s0 = smem + slot_off(0);
+      read_frags<Cfg, SWZ>(s0, s0 + Cfg::kABytes, 0, wm, wn, lane, fa[0], fb[0]);
     }
-    ring_wait_barrier_ng<L, S - 2, G>(min(S - 2, n_iter - 1), g0);
-    read_frags<Cfg, SWZ>(smem, smem + Cfg::kABytes, 0, wm, wn, lane, fa[0], fb[0]);
-  }
+  };
+  prologue_head();
+  prologue_tail();
 
   // ---- one K-step X.  V = 0: loads of steps X+S-1 (groups 1..F-1) and X+S
   // (group 0); V = 1: only those of step X+S-1; V = 2: none.
   auto step = [&](auto vc, int X) __attribute__((always_inline)) {
     constexpr int V = decltype(vc)::value;
-    const lds_u8* sa = smem + (X % S) * Cfg::kStageBytes;
+    const lds_u8* sa = smem + slot_off(X);
     constexpr_for<SUB>([&](auto kc_) __attribute__((always_inline)) {
       constexpr int kk = decltype(kc_)::value;
       constexpr int cur = kk & 1, nxt = cur ^ 1;
@@ -240,7 +275,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
       const int Y = kLast ? X + S : X + S - 1;
       // fragments read during this substep: substep kk+1 of step X, or
       // substep 0 of step X+1 once it is published
-      const lds_u8* ra = kLast ? smem + ((X + 1) % S) * Cfg::kStageBytes : sa;
+      const lds_u8* ra = kLast ? smem + slot_off(X + 1) : sa;
       constexpr int rkk = kLast ? 0 : kk + 1;
       const bool reads = !kLast || V <= 1 || X + 1 < n_iter;
       // MFMAs of this substep that run before the barrier (kLast only)
@@ -328,17 +363,47 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
     });
   };
 
-  int X = 0;
-  for (; X < n_iter - S; ++X) step(std::integral_constant<int, 0>{}, X);
-  if (n_iter >= S) {
-    step(std::integral_constant<int, 1>{}, X);
-    ++X;
-  }
-  for (; X < n_iter; ++X) step(std::integral_constant<int, 2>{}, X);
+  // The unit's main loop, from its first fragments to its last MFMA.
+  auto run_unit = [&]() __attribute__((always_inline)) {
+    prologue_wait();
+    int X = 0;
+    for (; X < n_iter - S; ++X) step(std::integral_constant<int, 0>{}, X);
+    if (n_iter >= S) {
+      step(std::integral_constant<int, 1>{}, X);
+      ++X;
+    }
+    for (; X < n_iter; ++X) step(std::integral_constant<int, 2>{}, X);
+    if constexpr (MF == 16) mfma16_settle();
+  };
 
-  if constexpr (MF == 16) mfma16_settle();
-  finish_tile<Cfg, kStore, kSplit>(a, smem, wave, m0, n0, acc, m0 + wm * Cfg::kWaveM,
-                                   n0 + wn * Cfg::kWaveN, lane, split);
+  if constexpr (!kPersist) {
+    run_unit();
+    finish_tile<Cfg, kStore, kSplit>(a, smem, wave, m0, n0, acc, m0 + wm * Cfg::kWaveM,
+                                     n0 + wn * Cfg::kWaveN, lane, split);
+  } else {
+    for (;;) {
+      run_unit();
+      // C of this unit drains through slot 0 while the next unit's steps
+      // 0 .. S-2 land in slots 1 .. S-1.
+      const int em0 = m0, en0 = n0;
+      const int next = unit + (int)gridDim.x;
+      const bool more = next < units;
+      // every wave is done with the ring (its last fragments are read)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (more) {
+        setup(next);
+        prologue_head();
+      }
+      finish_tile<Cfg, kStore, false, Cfg::kStageBytes, false>(
+          a, smem, wave, em0, en0, acc, em0 + wm * Cfg::kWaveM, en0 + wn * Cfg::kWaveN, lane, 0);
+      if (!more) return;
+      // every wave has read its staged rows back before slot 0 is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      prologue_tail();
+      unit = next;
+      zero_acc();
+    }
+  }
 }
 
 }  // namespace gemm

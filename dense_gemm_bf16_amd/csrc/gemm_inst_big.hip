@@ -2,6 +2,7 @@
 // bf16 operands, whole K-steps; also the dispatch.
 #define GEMM_SPLIT_PARAMS GEMM_BIG_PARAMS
 #define GEMM_SPLIT_RAGGED_APART
+#define GEMM_SPLIT_PERSIST
 #define GEMM_SPLIT_OWN 0
 #include "gemm_inst_split.hpp"
 #define GEMM_INST_big GEMM_DO_INST

@@ -2,5 +2,6 @@
 // fp16 operands, K % BK != 0.
 #define GEMM_SPLIT_PARAMS GEMM_BIG_PARAMS
 #define GEMM_SPLIT_RAGGED_APART
+#define GEMM_SPLIT_PERSIST
 #define GEMM_SPLIT_OWN 24
 #include "gemm_inst_split.hpp"

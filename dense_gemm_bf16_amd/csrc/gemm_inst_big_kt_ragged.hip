@@ -2,5 +2,6 @@
 // bf16 operands, K % 8 != 0.
 #define GEMM_SPLIT_PARAMS GEMM_BIG_PARAMS
 #define GEMM_SPLIT_RAGGED_APART
+#define GEMM_SPLIT_PERSIST
 #define GEMM_SPLIT_OWN 20
 #include "gemm_inst_split.hpp"

@@ -6,10 +6,10 @@
 
 #include "gemm_launch.hpp"
 
-#define GEMM_DO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16)   \
-  template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16>( \
+#define GEMM_DO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT)   \
+  template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT>( \
       const KernelArgs&, int, hipStream_t, int);
-#define GEMM_NO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16)
+#define GEMM_NO_INST(BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT)
 
 #ifndef GEMM_INST_big
 #define GEMM_INST_big GEMM_NO_INST
@@ -91,8 +91,8 @@
 #endif
 
 namespace gemm {
-#define GEMM_INSTANTIATE(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU) \
-  GEMM_INST_##TU(BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16)
+#define GEMM_INSTANTIATE(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT, TU) \
+  GEMM_INST_##TU(BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT)
 GEMM_TILE_CONFIGS(GEMM_INSTANTIATE)
 #undef GEMM_INSTANTIATE
 }  // namespace gemm

@@ -14,7 +14,9 @@
 // GEMM_SPLIT_RAGGED_APART defined, the three ragged-K kernels (K % 8 != 0)
 // of each K-tail group go to one more file each, GEMM_SPLIT_OWN 20 (bf16)
 // or 28 (fp16), as they would otherwise make the K-tail files the longest
-// of the build.
+// of the build.  With GEMM_SPLIT_PERSIST defined (rows built with
+// kOptPersist), the persistent-grid groups (kPersistent, with and without
+// kPartialK) are instantiated by the files with GEMM_SPLIT_OWN 32 and 48.
 #pragma once
 
 #include "gemm_launch.hpp"
@@ -41,6 +43,19 @@
 namespace gemm {
 static_assert(kF16 == 8 && kPartialK == 16 && kRaggedK == 4,
               "GEMM_SPLIT_OWN numbers the groups by these bits");
+static_assert(kPersistent == 32, "GEMM_SPLIT_OWN 32 and 48 name the persistent groups");
+#ifdef GEMM_SPLIT_PERSIST
+#if GEMM_SPLIT_OWN == 32
+GEMM_SPLIT_VARIANT(32)
+#else
+extern GEMM_SPLIT_VARIANT(32)
+#endif
+#if GEMM_SPLIT_OWN == 48
+GEMM_SPLIT_VARIANT(48)
+#else
+extern GEMM_SPLIT_VARIANT(48)
+#endif
+#endif
 #ifdef GEMM_SPLIT_RAGGED_APART
 #if GEMM_SPLIT_OWN == 20
 GEMM_SPLIT_RAGGED(16)

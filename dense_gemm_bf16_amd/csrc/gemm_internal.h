@@ -20,6 +20,7 @@ struct TileConfig {
   int threads;       // workgroup size
   int lds_bytes;     // static LDS per workgroup
   bool f16;          // also built for fp16 operands
+  bool persist;      // also built for a persistent grid (bf16 operands)
   hipError_t (*launch)(const KernelArgs&, int grid, hipStream_t, int flags);
 };
 
@@ -33,7 +34,8 @@ struct Plan {
   const TileConfig* tile;
   int splits;
   int group_m;
-  int k_rot;  // K-step rotation stride per tile, 0 = none
+  int k_rot;    // K-step rotation stride per tile, 0 = none
+  int persist;  // persistent grid of this many workgroups (a multiple of 8), 0 = none
   char name[64];
 };
 

@@ -61,28 +61,42 @@ constexpr bool has_partial_variant(int pipe) { return pipe == 8 || pipe == 9 || 
 
 // The (kOutF32, kSplitK, kRaggedK) combinations that occur, with the fixed
 // bits E (kF16, kPartialK).
+// A persistent grid has only the bf16-output kernels: it never splits K,
+// and the fp32 debug output of a persistent plan comes from the ordinary
+// kernel (same tiles, same per-tile K order, so the same sums).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
 hipError_t launch_variant(const KernelArgs& a, int grid, hipStream_t s, int flags) {
-  switch (flags & 7) {
-    case 0: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 0>(a, grid, s);
-    case 1: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 1>(a, grid, s);
-    case 2: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 2>(a, grid, s);
-    default: break;
-  }
-  // K % 8 != 0 (the direct-to-LDS and small-M kernels handle it only in
-  // their K % BK != 0 variant, which every such K selects)
-  if constexpr (!has_partial_variant(PIPE) || (E & kPartialK) != 0) {
+  if constexpr ((E & kPersistent) != 0) {
     switch (flags & 7) {
-      case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
-      case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 5>(a, grid, s);
-      default: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 6>(a, grid, s);
+      case 0: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 0>(a, grid, s);
+      case 4:
+        if constexpr ((E & kPartialK) != 0)
+          return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
     }
+  } else {
+    switch (flags & 7) {
+      case 0: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 0>(a, grid, s);
+      case 1: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 1>(a, grid, s);
+      case 2: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 2>(a, grid, s);
+      default: break;
+    }
+    // K % 8 != 0 (the direct-to-LDS and small-M kernels handle it only in
+    // their K % BK != 0 variant, which every such K selects)
+    if constexpr (!has_partial_variant(PIPE) || (E & kPartialK) != 0) {
+      switch (flags & 7) {
+        case 4: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 4>(a, grid, s);
+        case 5: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 5>(a, grid, s);
+        default: return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | 6>(a, grid, s);
+      }
+    }
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
-// Operand type E (0 or kF16) and, for the direct-to-LDS and small-M
-// kernels, kPartialK.
+// Operand type E (0 or kF16, with kPersistent for a persistent grid) and,
+// for the direct-to-LDS and small-M kernels, kPartialK.
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
 hipError_t launch_partial(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   if constexpr (has_partial_variant(PIPE)) {
@@ -92,12 +106,25 @@ hipError_t launch_partial(const KernelArgs& a, int grid, hipStream_t s, int flag
   return launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E>(a, grid, s, flags);
 }
 
-// F16: also instantiate the fp16-operand kernels.
-template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, bool F16>
+// What a configuration row builds beyond the bf16 kernels (its OPT mask).
+enum : int {
+  kOptF16 = 1,      // the fp16-operand kernels
+  kOptPersist = 2,  // the persistent-grid kernels, bf16 operands (direct-to-LDS only)
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int OPT>
 hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   if (flags & kSplitK) flags &= ~kOutF32;  // split slices always write fp32 partials
+  if (flags & kPersistent) {
+    if constexpr ((OPT & kOptPersist) != 0) {
+      static_assert(PIPE == 8 || PIPE == 10, "only the direct-to-LDS kernel walks tiles");
+      if ((flags & (kF16 | kSplitK | kOutF32)) == 0)
+        return launch_partial<BM, BN, BK, WM, WN, ST, SWZ, PIPE, kPersistent>(a, grid, s, flags);
+    }
+    return hipErrorInvalidValue;
+  }
   if (flags & kF16) {
-    if constexpr (F16)
+    if constexpr ((OPT & kOptF16) != 0)
       return launch_partial<BM, BN, BK, WM, WN, ST, SWZ, PIPE, kF16>(a, grid, s, flags);
     else
       return hipErrorInvalidValue;
@@ -106,8 +133,9 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 }
 
 // Built configurations, one row each:
-//   X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ, PIPE, F16, TU)
-// where F16 = 1 also builds the row for fp16 operands and TU names the
+//   X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ, PIPE, OPT, TU)
+// where OPT is a mask of kOptF16 (also build the row for fp16 operands) and
+// kOptPersist (also build its persistent-grid kernels), and TU names the
 // gemm_inst_<TU>.hip file that instantiates it.  A row whose parameters
 // are also needed elsewhere (the files that split its kernel variants over
 // several translation units) takes them from a GEMM_*_PARAMS macro, through
@@ -124,7 +152,7 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 #define GEMM_BIG_PARAMS 256, 256, 64, 2, 2, 2, 3, 10
 #define GEMM_MID_PARAMS 256, 128, 64, 2, 2, 3, 3, 10
 #define GEMM_PRODUCT_CONFIGS(X)                                        \
-  GEMM_ROW(X, t256x256x64_w2x2_s2_x3_p10, GEMM_BIG_PARAMS, 1, big)     \
+  GEMM_ROW(X, t256x256x64_w2x2_s2_x3_p10, GEMM_BIG_PARAMS, 3, big)     \
   GEMM_ROW(X, t256x128x64_w2x2_s3_x3_p10, GEMM_MID_PARAMS, 1, mid)     \
   X(t128x128x64_w2x2_s4_x3_p10, 128, 128, 64, 2, 2, 4, 3, 10, 1, mid128) \
   X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 1, smallm)     \
@@ -171,8 +199,8 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 
 #define GEMM_TILE_CONFIGS(X) GEMM_PRODUCT_CONFIGS(X) GEMM_ABLATION_CONFIGS(X)
 
-#define GEMM_DECLARE_LAUNCH(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16, TU) \
-  extern template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F16>(  \
+#define GEMM_DECLARE_LAUNCH(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT, TU) \
+  extern template hipError_t launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT>(  \
       const KernelArgs&, int, hipStream_t, int);
 GEMM_TILE_CONFIGS(GEMM_DECLARE_LAUNCH)
 #undef GEMM_DECLARE_LAUNCH

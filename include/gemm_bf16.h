@@ -110,10 +110,21 @@ int gemm_bf16_ex(const char* config,
 
 /* Name of the configuration gemm_bf16 (and gemm_f16: the shape rules are the
  * same for both operand types) would choose for this shape, e.g.
- * "t256x256x64_w2x2_s2_x2_p6_k1_g4": tile BM x BN x BK, waves, ring stages,
+ * "t256x256x64_w2x2_s2_x3_p10_k1_g4": tile BM x BN x BK, waves, ring stages,
  * LDS swizzle, load schedule, then K splits and GROUP_M (and "_r<n>", the
  * K-step rotation, when on).  Per-thread static storage, valid until the
- * thread's next call; never NULL. */
+ * thread's next call; never NULL.
+ *
+ * gemm_bf16_ex also accepts a "_P<n>" suffix on the tile built for it
+ * (t256x256x64_w2x2_s2_x3_p10): a persistent grid of n workgroups (rounded
+ * down to a multiple of 8, at most the tile count) that walk the tiles in
+ * the same order, each draining one tile's C through one LDS ring slot
+ * while the next tile's first K-steps load into the others.  Same tiles and
+ * per-tile summation order, so the same bits as the plan without it.  bf16
+ * operands only, never with a split ("_k1"); its fp32 output runs the
+ * ordinary kernel (same sums).  This is the persistent scheduling of "Matrix
+ * Multiplication on NVIDIA's Blackwell" (Kernels 7 and 8: double-buffered
+ * output, persistent kernel), re-designed for one LDS ring per CU. */
 const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K);
 
 /* Enumerate the built configurations: the i-th name, or NULL past the end. */

@@ -92,6 +92,25 @@ def test_argument_checks_need_no_device(lib):
                               None) == lib.GEMM_ERR_UNSUPPORTED
 
 
+def test_persistent_plan_names_on_the_host(lib):
+    """Plan names with a persistent grid (_P<n>): accepted for the tile built
+    with it (M = 0, so nothing is launched), refused with a split, on a tile
+    not built for it, and for fp16 operands."""
+    so = lib._lib
+    fake = ctypes.c_void_p(0x10000)
+
+    def rc(name, half=False):
+        fn = so.gemm_f16_ex if half else so.gemm_bf16_ex
+        return fn(name.encode(), 0, 8192, 8192, fake, 8192, fake, 8192, fake, 8192, 0, None)
+
+    big = "t256x256x64_w2x2_s2_x3_p10"
+    assert rc(big + "_k1_g4_P256") == lib.GEMM_OK
+    assert rc(big + "_k1_g8_r1_P64") == lib.GEMM_OK
+    assert rc(big + "_k2_g4_P256") == lib.GEMM_ERR_UNSUPPORTED
+    assert rc("t256x128x64_w2x2_s3_x3_p10_k1_g4_P256") == lib.GEMM_ERR_UNSUPPORTED
+    assert rc(big + "_k1_g4_P256", half=True) == lib.GEMM_ERR_UNSUPPORTED
+
+
 def test_config_names(lib):
     names = lib.config_names()
     assert len(names) == len(set(names)) >= 2

@@ -323,3 +323,73 @@ def test_ablation_configurations_when_built():
             assert check_bf16(got, ref16, None, K, exact=True)["ok"], cfg + suffix
             got32 = run_gemm(A, B, config=cfg + suffix, out_f32=True)
             assert check_f32(got32, ref64, K, exact=True)["ok"], cfg + suffix
+
+
+# ------------------------------------------------------ persistent grid
+
+BIG = "t256x256x64_w2x2_s2_x3_p10"
+
+
+@pytest.mark.parametrize("shape,plan", [
+    ((1024, 1024, 512), "_k1_g4_P8"),        # 16 tiles on 8 workgroups: 2 each
+    ((600, 1100, 456), "_k1_g4_P8"),         # ragged M, N, K: edge tiles in the walk
+    ((1100, 2100, 520), "_k1_g8_r1_P16"),    # rotation, GROUP_M 8, 45 tiles on 16
+])
+def test_persistent_plan_bit_exact(shape, plan):
+    """A persistent grid (each workgroup walks several tiles; C of one tile
+    drains through one LDS slot while the next tile's first K-steps land in
+    the others) on integer inputs: bf16 bit-exact, and the fp32 debug output
+    (the ordinary kernel, same per-tile order) exact."""
+    M, N, K = shape
+    A = int_bf16(M, K, seed=1300 + M)
+    B = int_bf16(N, K, seed=1301 + N)
+    ref16, ref64 = _oracle().gemm(A, B)
+    name = BIG + plan
+    got = run_gemm(A, B, config=name)
+    rep = check_bf16(got, ref16, None, K, exact=True)
+    print(shape, name, rep, flush=True)
+    assert rep["ok"], rep
+    got32 = run_gemm(A, B, config=name, out_f32=True)
+    assert check_f32(got32, ref64, K, exact=True)["ok"]
+
+
+def test_persistent_plan_k_not_multiple_of_8():
+    """K = 203 with NaN in the padding: the tail chunk is trimmed in the slot
+    its step lands in, which the persistent grid shifts by one."""
+    M, N, K = 520, 600, 203
+    ld = 216
+    A = np.full((M, ld), 0x7FC0, np.uint16)
+    B = np.full((N, ld), 0x7FC0, np.uint16)
+    A[:, :K] = int_bf16(M, K, seed=1310)
+    B[:, :K] = int_bf16(N, K, seed=1311)
+    ref16, _ = _oracle().gemm(A, B, K=K)
+    got = run_gemm(A, B, K=K, config=BIG + "_k1_g4_P8")
+    assert check_bf16(got, ref16, None, K, exact=True)["ok"]
+
+
+def test_persistent_plan_matches_one_tile_per_workgroup_on_prefill():
+    """M = 8192 prefill attention-out (1024 tiles, 4 per workgroup on a grid
+    of 256): the same bits as the ordinary plan on N(0,1) data, since each
+    tile sums its K-steps in the same order; sampled rows against the
+    oracle."""
+    w = WORKLOADS["prefill_attn_out"]
+    A, B = w.make()
+    got = run_gemm(A, B, config=BIG + "_k1_g4_P256")
+    ref = run_gemm(A, B, config=BIG + "_k1_g4")
+    assert np.array_equal(got, ref), int(np.count_nonzero(got != ref))
+    rows = np.array([0, 1, 255, 256, 4095, 4096, 8191])
+    r16, r64 = _oracle().gemm(np.ascontiguousarray(A[rows]), B, K=w.K)
+    rep = check_bf16(got[rows], r16, r64, w.K, w.sigma_a, w.sigma_b)
+    assert rep["ok"], rep
+
+
+def test_persistent_plan_k_zero():
+    import torch
+
+    import dense_gemm_bf16_amd as g
+
+    C = torch.full((300, 600), 1234, dtype=torch.int16, device="cuda")
+    dummy = torch.zeros(8, dtype=torch.int16, device="cuda")
+    g.gemm_bf16_ex(BIG + "_k1_g4_P8", 300, 600, 0, dummy, 8, dummy, 8, C, 600)
+    torch.cuda.synchronize()
+    assert not C.cpu().numpy().any()
