@@ -24,6 +24,8 @@ GEMM_ERR_MISALIGNED = 2
 GEMM_ERR_UNSUPPORTED = 3
 GEMM_ERR_HIP = 4
 GEMM_ERR_CAPTURE = 5
+GEMM_ERR_SCRATCH = 6
+GEMM_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -72,6 +74,9 @@ _lib.gemm_f16_ex.argtypes = [ctypes.c_char_p, _i64, _i64, _i64, _p, _i64, _p, _i
                              _p, _i64, ctypes.c_int, _p]
 _lib.gemm_f16_config_at.restype = ctypes.c_char_p
 _lib.gemm_f16_config_at.argtypes = [ctypes.c_int]
+_lib.gemm_bf16_ex_noalloc.restype = ctypes.c_int
+_lib.gemm_bf16_ex_noalloc.argtypes = [ctypes.c_char_p, _i64, _i64, _i64, _p, _i64, _p, _i64,
+                                      _p, _i64, ctypes.c_int, _p]
 
 
 class GemmError(RuntimeError):
@@ -146,6 +151,15 @@ def gemm_f16_ex(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32=False,
     cfg = None if config is None else config.encode()
     _check(_lib.gemm_f16_ex(cfg, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
                             1 if out_f32 else 0, _stream(stream)))
+
+
+def gemm_bf16_ex_noalloc(config, M, N, K, A, lda, B, ldb, C, ldc, out_f32=False,
+                         stream=None) -> None:
+    """As gemm_bf16_ex, with the split-K partials in the library's static
+    scratch array instead of an allocated workspace (nothing is allocated)."""
+    cfg = None if config is None else config.encode()
+    _check(_lib.gemm_bf16_ex_noalloc(cfg, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                     1 if out_f32 else 0, _stream(stream)))
 
 
 def gemm_bf16_status(M, N, K, A, lda, B, ldb, C, ldc, stream=0, out_f32=False,

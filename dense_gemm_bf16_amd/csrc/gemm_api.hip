@@ -289,9 +289,12 @@ int check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   return GEMM_OK;
 }
 
+// `fixed_ws`: the device address of a caller-side partial buffer of
+// `fixed_bytes` bytes to use instead of the per-stream workspace (the
+// no-allocation entry point), or NULL.
 int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
         const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
-        hipStream_t stream) {
+        hipStream_t stream, void* fixed_ws = nullptr, size_t fixed_bytes = 0) {
   const TileConfig& t = *p.tile;
   if (half && !t.f16) return GEMM_ERR_UNSUPPORTED;
   if (p.persist > 0 && (half || !t.persist || p.splits > 1)) return GEMM_ERR_UNSUPPORTED;
@@ -336,11 +339,17 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   if (p.persist > 0 && !out_f32) flags |= kPersistent;
   void* ws = nullptr;
   if (p.splits > 1) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e);
-    int rc = get_workspace(dev, stream, workspace_bytes(p, M, N), &ws);
-    if (rc != GEMM_OK) return rc;
+    const size_t need = workspace_bytes(p, M, N);
+    if (fixed_ws) {
+      if (need > fixed_bytes) return GEMM_ERR_SCRATCH;
+      ws = fixed_ws;
+    } else {
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return hip_fail(e);
+      int rc = get_workspace(dev, stream, need, &ws);
+      if (rc != GEMM_OK) return rc;
+    }
     a.part = (float*)ws;
     a.ldp = partial_ld(N);
     a.part_stride = M * a.ldp;
@@ -376,6 +385,39 @@ int gemm_entry(const char* config, int64_t M, int64_t N, int64_t K, const void* 
   rc = make_plan(config, M, N, K, half, &p);
   if (rc != GEMM_OK) return rc;
   return run(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32, half, (hipStream_t)stream);
+}
+
+// ------------------------------------------------- static scratch (no-alloc)
+// The no-allocation entry point keeps its split-K partials in this array.
+// Each device that loads the library holds its own copy, at its own
+// address, until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up
+// once per device (hipGetSymbolAddress with that device current) and only
+// that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = GEMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return GEMM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GEMM_OK;
 }
 
 // The i-th table entry with f16 set (or with no condition), or NULL.
@@ -427,6 +469,23 @@ int gemm_f16_ex(const char* config, int64_t M, int64_t N, int64_t K, const void*
 
 const char* gemm_f16_config_at(int i) { return gemm::config_at(i, true); }
 
+int gemm_bf16_ex_noalloc(const char* config, int64_t M, int64_t N, int64_t K, const void* A,
+                         int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                         int out_f32, void* stream) {
+  int rc = gemm::check_args(M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != GEMM_OK) return rc;
+  gemm::Plan p{};
+  rc = gemm::make_plan(config, M, N, K, false, &p);
+  if (rc != GEMM_OK) return rc;
+  if (gemm::workspace_bytes(p, M, N) > gemm::kScratchBytes) return GEMM_ERR_SCRATCH;
+  if (M == 0 || N == 0) return GEMM_OK;
+  void* ws = nullptr;
+  rc = gemm::scratch_of_current_device(&ws);
+  if (rc != GEMM_OK) return rc;
+  return gemm::run(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32 != 0, false,
+                   (hipStream_t)stream, ws, gemm::kScratchBytes);
+}
+
 const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return "invalid";
   gemm::Plan p = gemm::choose_plan(M, N, K);
@@ -448,7 +507,9 @@ const char* gemm_bf16_status_string(int status) {
     case GEMM_ERR_CAPTURE:
       return "the stream is being captured and this shape needs a larger split-K workspace than "
              "the one reserved for it (reserve it before capture)";
-
+    case GEMM_ERR_SCRATCH:
+      return "this plan's split-K partials exceed the static scratch of the no-allocation "
+             "entry point";
     default: return "unknown status";
   }
 }

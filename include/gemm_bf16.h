@@ -45,7 +45,8 @@
  * with calls that split K.  Allocation cannot be captured: pre-size the
  * workspace with gemm_bf16_reserve_workspace before stream capture; a call
  * under capture that would need to grow it returns GEMM_ERR_CAPTURE without
- * enqueueing anything.
+ * enqueueing anything.  gemm_bf16_ex_noalloc uses a static scratch array
+ * instead and never allocates.
  *
  * Streams and errors.  Calls are asynchronous: work is enqueued on `stream`
  * (a hipStream_t passed as void*, NULL = the null stream) and the call never
@@ -76,6 +77,8 @@ extern "C" {
 #define GEMM_ERR_CAPTURE 5     /* the stream is being captured and the call
                                   would have to allocate a larger split-K
                                   workspace (reserve it before capture) */
+#define GEMM_ERR_SCRATCH 6     /* gemm_bf16_ex_noalloc: the plan's split-K
+                                  partials exceed its static scratch */
 
 /* C = A * B^T with bf16 output.  Arguments as described above.  Returns a
  * status code. */
@@ -170,6 +173,29 @@ int gemm_f16_ex(const char* config,
 /* Enumerate the configurations built for fp16 operands: the i-th name, or
  * NULL past the end. */
 const char* gemm_f16_config_at(int i);
+
+/* ------------------------------------------------------- no allocation
+ * For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as gemm_bf16_ex (config NULL or "" = automatic, out_f32 as there,
+ * the same plans and summation order, so the same bits), but the split-K
+ * partials go to a static array of GEMM_NOALLOC_SCRATCH_BYTES that every
+ * device holds from the library's first use on it until the process ends,
+ * instead of the per-stream workspace.  It calls no hipMalloc or hipFree
+ * and never synchronises.  A plan whose partials (S * M * roundup8(N) * 4
+ * bytes) exceed the array is refused with GEMM_ERR_SCRATCH before anything
+ * is enqueued; the automatic plans of every shape stay below it.  Every
+ * call on one device shares that device's array, so calls that may overlap
+ * on one device (different streams, or concurrent graph replays) race and
+ * must be ordered by the caller; nothing in the array needs clearing
+ * between calls.  Returns a status code. */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gemm_bf16_ex_noalloc(const char* config,
+                         int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda,
+                         const void* B, int64_t ldb,
+                         void* C, int64_t ldc,
+                         int out_f32, void* stream);
 
 /* Human-readable text for a status code.  Static storage; never NULL. */
 const char* gemm_bf16_status_string(int status);

@@ -55,11 +55,11 @@ def test_binding_names_match_header(lib):
 
 def test_status_strings(lib):
     seen = set()
-    for code in range(6):
+    for code in range(7):
         s = lib.status_string(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 6
+    assert len(seen) == 7
     assert "captur" in lib.status_string(lib.GEMM_ERR_CAPTURE)
     assert lib.status_string(99) == "unknown status"
 
@@ -90,6 +90,34 @@ def test_argument_checks_need_no_device(lib):
                               None) == lib.GEMM_ERR_UNSUPPORTED
         assert so.gemm_f16_ex(n.encode(), 0, 8, 8, None, 8, None, 8, fake, 8, 0,
                               None) == lib.GEMM_ERR_UNSUPPORTED
+    # the no-allocation entry point: same argument checks, and a plan whose
+    # partials exceed its static scratch is refused on the host
+    assert so.gemm_bf16_ex_noalloc(None, -1, 8, 8, fake, 8, fake, 8, fake, 8, 0,
+                                   None) == lib.GEMM_ERR_INVALID_ARG
+    assert so.gemm_bf16_ex_noalloc(None, 8, 8, 8, odd, 8, fake, 8, fake, 8, 0,
+                                   None) == lib.GEMM_ERR_MISALIGNED
+    assert so.gemm_bf16_ex_noalloc(b"no_such_config", 8, 8, 8, fake, 8, fake, 8, fake, 8, 0,
+                                   None) == lib.GEMM_ERR_UNSUPPORTED
+    big_split = "t256x128x64_w2x2_s3_x3_p10_k16"  # 16 x 256 x 8192 x 4 B = 128 MiB
+    assert 16 * 256 * 8192 * 4 > lib.GEMM_NOALLOC_SCRATCH_BYTES
+    assert so.gemm_bf16_ex_noalloc(big_split.encode(), 256, 8192, 8192, fake, 8192, fake, 8192,
+                                   fake, 8192, 0, None) == lib.GEMM_ERR_SCRATCH
+    assert so.gemm_bf16_ex_noalloc(None, 0, 16, 8, None, 8, None, 8, fake, 16, 0,
+                                   None) == lib.GEMM_OK
+
+
+def test_noalloc_scratch_covers_every_automatic_plan(lib):
+    """The automatic plans' split-K partials stay below the static scratch
+    for every workload shape and a sweep of decode-like and ragged shapes,
+    so gemm_bf16_ex_noalloc refuses only forced plans."""
+    from synthetic_inputs import WORKLOADS
+
+    shapes = [(w.M, w.N, w.K) for w in WORKLOADS.values()]
+    for M in (1, 17, 64, 65, 128, 129, 200, 256, 300, 512, 1024):
+        for N in (128, 1000, 4096, 8192, 10240, 19200, 28672):
+            shapes.append((M, N, 8192))
+    for M, N, K in shapes:
+        assert lib.workspace_size(M, N, K) <= lib.GEMM_NOALLOC_SCRATCH_BYTES, (M, N, K)
 
 
 def test_persistent_plan_names_on_the_host(lib):
