@@ -162,7 +162,9 @@ def cpu_baseline(w, A, B, target_s: float, fmt: str = "bf16"):
 
 class ClockReader:
     """Shader and memory clocks of the GPU through amdsmi (None when amdsmi
-    or its metrics are not available)."""
+    or its metrics are not available).  The GPU metrics refresh about once a
+    second (their system_clock_counter steps by ~1 s), so a value is used
+    only if it was refreshed after the timed region began."""
 
     def __init__(self, torch):
         self.h = None
@@ -187,12 +189,6 @@ class ClockReader:
                     self.h = h
             if self.h is None and len(handles) == 1:
                 self.h = handles[0]
-            # the first metric reads of a process have returned stale values
-            # (idle-level clocks while a GEMM ran); read once before use
-            if self.h is not None:
-                for _ in range(3):
-                    self.sample()
-                    time.sleep(0.01)
         except Exception:
             self.h = None
 
@@ -209,9 +205,15 @@ class ClockReader:
 
         xcd = [num(v) for v in (m.get("current_gfxclks") or [])]
         xcd = [v for v in xcd if v is not None]
-        return {"gfx": xcd or ([num(m.get("current_gfxclk"))] if num(m.get("current_gfxclk"))
+        t = m.get("system_clock_counter")
+        return {"t": t if isinstance(t, int) else None,
+                "gfx": xcd or ([num(m.get("current_gfxclk"))] if num(m.get("current_gfxclk"))
                                else []),
                 "mem": num(m.get("current_uclk"))}
+
+    def stamp(self):
+        s = self.sample()
+        return None if s is None else s["t"]
 
 
 def summarize_clocks(samples):
@@ -274,20 +276,25 @@ def time_workload(g, torch, np, w, args, stream, clocks, config=None):
         for i in range(args.warmup):
             step(i)
     torch.cuda.synchronize()
+    t_begin = clocks.stamp() if clocks is not None else None
     us, wall = timed(args.steps)
     reps = [timed(args.steps)[0] for _ in range(args.repeats)]
 
-    # clocks while the same GEMM keeps the GPU busy, untimed
+    # clocks: the same GEMM keeps running, untimed, until the GPU metrics
+    # have been refreshed after the timed region began (at most --clock-s)
     samples = []
-    if clocks is not None and clocks.h is not None:
-        n_more = int(min(5000, max(50, args.clock_s * 1e6 / max(us, 1.0))))
-        done = torch.cuda.Event()
-        for i in range(n_more):
-            step(i)
-        done.record(stream)
-        while not done.query():
-            samples.append(clocks.sample())
-            time.sleep(0.005)
+    if clocks is not None and t_begin is not None:
+        batch = int(min(2000, max(1, 0.02 * 1e6 / max(us, 1.0))))  # ~20 ms of launches
+        t_stop = time.perf_counter() + args.clock_s
+        with torch.cuda.stream(stream):
+            while time.perf_counter() < t_stop:
+                s = clocks.sample()
+                if s is not None and s["t"] is not None and s["t"] > t_begin:
+                    samples.append(s)
+                    break
+                for i in range(batch):
+                    step(i)
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
 
     t = us * 1e-6
@@ -319,8 +326,9 @@ def main() -> int:
                     help="seconds of untimed launches before the warm-up (clock ramp)")
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra timings of --steps launches (min / median / max)")
-    ap.add_argument("--clock-s", type=float, default=0.05,
-                    help="seconds of untimed launches while the clocks are sampled")
+    ap.add_argument("--clock-s", type=float, default=1.5,
+                    help="at most this many seconds of untimed launches while waiting for "
+                         "a refresh of the GPU clock metrics")
     ap.add_argument("--workload", default="square4096_normal")
     ap.add_argument("--workloads", default="default",
                     help="the shapes of the 'workloads' object: 'default' (the prefill and "

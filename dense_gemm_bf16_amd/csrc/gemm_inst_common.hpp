@@ -26,6 +26,15 @@
 #ifndef GEMM_INST_skinny
 #define GEMM_INST_skinny GEMM_NO_INST
 #endif
+#ifndef GEMM_INST_big8
+#define GEMM_INST_big8 GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_big8b
+#define GEMM_INST_big8b GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_mid8
+#define GEMM_INST_mid8 GEMM_NO_INST
+#endif
 #ifndef GEMM_INST_a
 #define GEMM_INST_a GEMM_NO_INST
 #endif

@@ -165,7 +165,8 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 // measurements behind the product choices compared against -- LDS-DMA
 // spread issue (PIPE 1, 3, 4), ping-pong (2, 5), register-staged (6), the
 // 32x32x16 forms of the direct-to-LDS tiles (8), the unswizzled and
-// row-mod-8 LDS layouts (x0, x1).
+// row-mod-8 LDS layouts (x0, x1), and the direct-to-LDS tiles on 8 waves (two
+// per SIMD: 256 x 256 as 2 x 4 or 4 x 2 waves, 256 x 128 as 4 x 2).
 #ifdef GEMM_WITH_ABLATION
 #define GEMM_ABLATION_CONFIGS(X)                                  \
   X(t256x256x64_w2x2_s2_x2_p0, 256, 256, 64, 2, 2, 2, 2, 0, 0, a) \
@@ -192,7 +193,10 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t256x128x64_w2x2_s3_x2_p8, 256, 128, 64, 2, 2, 3, 2, 8, 1, v) \
   X(t128x128x64_w2x2_s4_x2_p8, 128, 128, 64, 2, 2, 4, 2, 8, 1, w) \
   X(t256x256x64_w2x2_s2_x0_p0, 256, 256, 64, 2, 2, 2, 0, 0, 0, j) \
-  X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, 0, j)
+  X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, 0, j) \
+  X(t256x256x64_w2x4_s2_x3_p10, 256, 256, 64, 2, 4, 2, 3, 10, 0, big8)   \
+  X(t256x256x64_w4x2_s2_x3_p10, 256, 256, 64, 4, 2, 2, 3, 10, 0, big8b)  \
+  X(t256x128x64_w4x2_s3_x3_p10, 256, 128, 64, 4, 2, 3, 3, 10, 0, mid8)
 #else
 #define GEMM_ABLATION_CONFIGS(X)
 #endif
