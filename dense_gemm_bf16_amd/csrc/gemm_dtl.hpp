@@ -50,11 +50,23 @@
 
 namespace gemm {
 
-template <int BM, int BN, int BK, int WM, int WN, int S, int SWZ, int FLAGS, int MF>
+// DL (B lead): B runs DL K-steps ahead of A.  The ring then has S slots
+// of A + B and DL more B-only slots; the loads of "stage" Y are A of step Y
+// and B of step Y + DL (an out-of-range load that reads zero into a free B
+// slot when Y + DL is past the end, so every stage issues the same loads and
+// the wait counts stay those of DL = 0), and the prologue first issues B of
+// steps 0 .. DL-1.  B comes from HBM in the memory-bound shapes while A
+// (the activations, shared by every tile of a K range) mostly comes from L2,
+// so this keeps more of B in flight per CU.
+template <int BM, int BN, int BK, int WM, int WN, int S, int SWZ, int FLAGS, int MF, int DL = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64),
                           amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void
 gemm_bf16_dtl_kernel(KernelArgs a) {
   using Cfg = TileCfg<BM, BN, BK, WM, WN, S, SWZ, MF>;
+  static_assert(DL >= 0, "B lead");
+  constexpr int SB = S + DL;  // B slots
+  constexpr int kRingBytes = S * Cfg::kStageBytes + DL * Cfg::kBBytes;
+  static_assert(kRingBytes <= 160 * 1024, "LDS is 160 KB per CU");
   constexpr int T = Cfg::kThreads;
   constexpr int CPR = Cfg::kCpr;
   constexpr int SUB = Cfg::kSub;
@@ -76,7 +88,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   static_assert(L % F == 0, "equal load groups");
   static_assert((S - 2) * L + L / F < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kRingBytes];
   lds_u8* const smem = (lds_u8*)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
@@ -93,6 +105,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   // of one workgroup per unit.
   constexpr bool kPersist = (FLAGS & kPersistent) != 0;
   static_assert(!(kPersist && kSplit), "a persistent grid does not split K");
+  static_assert(!(kPersist && DL > 0), "a persistent grid has no B lead");
   const int ntiles = a.tiles_m * a.tiles_n;
   const int units = kSplit ? ntiles * a.splits : ntiles;
   const int full_tiles = a.K / BK;  // K-steps wholly inside K
@@ -151,16 +164,36 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
     return (uint32_t)(((kPersist ? Y + 1 : Y) % S) * Cfg::kStageBytes);
   };
 
-  // LDS byte offset (within a slot) of load i's 1 KB of this wave.
-  auto lds_off = [&](int i) __attribute__((always_inline)) {
-    return (uint32_t)((i < LA ? 0 : Cfg::kABytes) + ((i < LA ? i : i - LA) * T + wave * 64) * 16);
+  // Byte offset of the B tile of K-step Y: in its step's slot when DL = 0,
+  // else in a ring of S + DL B slots (the first S inside the A + B slots).
+  auto b_off = [&](int Y) __attribute__((always_inline)) {
+    if constexpr (DL == 0) {
+      return slot_off(Y) + (uint32_t)Cfg::kABytes;
+    } else {
+      const int j = Y % SB;
+      return (uint32_t)(j < S ? j * Cfg::kStageBytes + Cfg::kABytes
+                              : S * Cfg::kStageBytes + (j - S) * Cfg::kBBytes);
+    }
   };
 
-  // Load i of step Y (Y < n_iter).
+  // LDS byte offset (within its operand tile) of load i's 1 KB of this wave.
+  auto lds_off = [&](int i) __attribute__((always_inline)) {
+    return (uint32_t)(((i < LA ? i : i - LA) * T + wave * 64) * 16);
+  };
+
+  // Load i of stage Y (Y < n_iter): A of step Y, or B of step Y + DL.
   auto dma_one = [&](int Y, int i) __attribute__((always_inline)) {
-    const int kt = korder.kt(Y);
-    const uint32_t dst = smem_addr + slot_off(Y) + lds_off(i);
-    const u32x4& rs = i < LA ? rsrc_a : rsrc_b;
+    const bool is_a = i < LA;
+    const int YS = is_a ? Y : Y + DL;  // the K-step this load belongs to
+    const uint32_t dst = smem_addr + (is_a ? slot_off(Y) : b_off(YS)) + lds_off(i);
+    const u32x4& rs = is_a ? rsrc_a : rsrc_b;
+    if constexpr (DL > 0) {
+      if (YS >= n_iter) {  // past the end: keep the stage's load count
+        dma16(rs, dst, kOOB, 0u);
+        return;
+      }
+    }
+    const int kt = korder.kt(YS);
     if constexpr (kPartial) {
       if (kt >= full_tiles) {
         const int k0 = kt * BK;
@@ -173,17 +206,16 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
     dma16(rs, dst, voff[i], (uint32_t)(kt * BK * 2));
   };
 
-  // Trim the chunk that straddles K in this thread's part of step Y's slot
-  // (after its loads have landed).
+  // Trim the chunk that straddles K in this thread's part of step Y's A and
+  // B tiles (after their loads have landed).
   auto trim_tail = [&](int Y) __attribute__((always_inline)) {
     const int k0 = korder.kt(Y) * BK;
-    lds_u8* slot = smem + slot_off(Y);
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int ii = i < LA ? i : i - LA;
       const int keep = a.K - (k0 + chunk2[ii & 1] * 8);
       if (keep > 0 && keep < 8) {
-        lds_u32x4* p = (lds_u32x4*)(slot + (i < LA ? 0 : Cfg::kABytes) + (ii * T + tid) * 16);
+        lds_u32x4* p = (lds_u32x4*)(smem + (i < LA ? slot_off(Y) : b_off(Y)) + (ii * T + tid) * 16);
         u32x4 v = *p;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -195,6 +227,13 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
     }
   };
 
+  // With a B lead, the wait for step Y leaves the B loads of stage Y (B of
+  // step Y + DL, the last LB loads that stage issues) in flight: loads land
+  // in order, so the count still proves that A of step Y and everything
+  // issued before it (B of step Y came with stage Y - DL) have landed.
+  constexpr int kLeadSlack = DL > 0 ? L - LA : 0;
+  static_assert((S - 2) * L + L / F + kLeadSlack < 64, "vmcnt range");
+
   // Wait until step Y's loads have landed in every wave and publish them;
   // `later` steps after Y (whole) may still be in flight.
   auto publish = [&](int Y, int later) __attribute__((always_inline)) {
@@ -204,7 +243,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
         trim_tail(Y);
       }
     }
-    ring_wait_barrier_n<L, S - 2>(later);
+    ring_wait_barrier_n_off<L, S - 2, kLeadSlack>(later);
   };
 
   typename Cfg::Acc acc[Cfg::kFragM][Cfg::kFragN];
@@ -229,6 +268,13 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   // then wait for step 0 and read its first fragments --------------------
   constexpr int G = L / F;
   auto prologue_head = [&]() __attribute__((always_inline)) {
+    if constexpr (DL > 0) {  // B of steps 0 .. DL-1 (later B comes with the stages)
+#pragma unroll
+      for (int p = 0; p < DL; ++p)
+        if (p < n_iter)
+#pragma unroll
+          for (int i = LA; i < L; ++i) dma_one(p - DL, i);
+    }
 #pragma unroll
     for (int p = 0; p + 1 < S; ++p)
       if (p < n_iter)
@@ -252,9 +298,8 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
           trim_tail(0);
         }
       }
-      ring_wait_barrier_ng<L, S - 2, G>(min(S - 2, n_iter - 1), S - 1 < n_iter);
-      const lds_u8* s0 = smem + slot_off(0);
-      read_frags<Cfg, SWZ>(s0, s0 + Cfg::kABytes, 0, wm, wn, lane, fa[0], fb[0]);
+      ring_wait_barrier_ng<L, S - 2, G, kLeadSlack>(min(S - 2, n_iter - 1), S - 1 < n_iter);
+      read_frags<Cfg, SWZ>(smem + slot_off(0), smem + b_off(0), 0, wm, wn, lane, fa[0], fb[0]);
     }
   };
   prologue_head();
@@ -265,6 +310,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   auto step = [&](auto vc, int X) __attribute__((always_inline)) {
     constexpr int V = decltype(vc)::value;
     const lds_u8* sa = smem + slot_off(X);
+    const lds_u8* sb = smem + b_off(X);
     constexpr_for<SUB>([&](auto kc_) __attribute__((always_inline)) {
       constexpr int kk = decltype(kc_)::value;
       constexpr int cur = kk & 1, nxt = cur ^ 1;
@@ -276,6 +322,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
       // fragments read during this substep: substep kk+1 of step X, or
       // substep 0 of step X+1 once it is published
       const lds_u8* ra = kLast ? smem + slot_off(X + 1) : sa;
+      const lds_u8* rb = kLast ? smem + b_off(X + 1) : sb;
       constexpr int rkk = kLast ? 0 : kk + 1;
       const bool reads = !kLast || V <= 1 || X + 1 < n_iter;
       // MFMAs of this substep that run before the barrier (kLast only)
@@ -328,7 +375,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
                 constexpr int at = r < FM ? pos_a(r) : pos_b(r - FM);
                 if constexpr ((at < NM - 1 ? at : NM - 1) == j) {
                   if (reads)
-                    read_frag_one<Cfg, SWZ, r>(ra, ra + Cfg::kABytes, rkk, wm, wn, lane, fa[0],
+                    read_frag_one<Cfg, SWZ, r>(ra, rb, rkk, wm, wn, lane, fa[0],
                                                fb[nxt]);
                   __builtin_amdgcn_sched_barrier(0);
                 }
@@ -354,7 +401,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
               if constexpr (rn > rb) {
                 if (reads)
                   read_frag_one<Cfg, SWZ, frag_need_order<Cfg>(rb)>(
-                      ra, ra + Cfg::kABytes, rkk, wm, wn, lane, fa[na], fb[nxt]);
+                      ra, rb, rkk, wm, wn, lane, fa[na], fb[nxt]);
               } else {
                 dma_one(Y, grp * G + (p - rb));
               }

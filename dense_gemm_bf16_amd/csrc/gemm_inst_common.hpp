@@ -26,6 +26,12 @@
 #ifndef GEMM_INST_skinny
 #define GEMM_INST_skinny GEMM_NO_INST
 #endif
+#ifndef GEMM_INST_midb1
+#define GEMM_INST_midb1 GEMM_NO_INST
+#endif
+#ifndef GEMM_INST_midb2
+#define GEMM_INST_midb2 GEMM_NO_INST
+#endif
 #ifndef GEMM_INST_big8
 #define GEMM_INST_big8 GEMM_NO_INST
 #endif

@@ -166,12 +166,12 @@ __device__ __forceinline__ void ring_wait_barrier_n(int n) {
   ring_wait_barrier_n_off<STEP, MAXN, 0>(n);
 }
 
-// ring_wait_barrier<STEP * n + (g ? G : 0)> for run-time n in [0, MAXN]
-// and a run-time flag g.
-template <int STEP, int MAXN, int G>
+// ring_wait_barrier<STEP * n + (g ? G : 0) + OFF> for run-time n in
+// [0, MAXN] and a run-time flag g.
+template <int STEP, int MAXN, int G, int OFF = 0>
 __device__ __forceinline__ void ring_wait_barrier_ng(int n, bool g) {
-  if (g) ring_wait_barrier_n_off<STEP, MAXN, G>(n);
-  else ring_wait_barrier_n<STEP, MAXN>(n);
+  if (g) ring_wait_barrier_n_off<STEP, MAXN, G + OFF>(n);
+  else ring_wait_barrier_n_off<STEP, MAXN, OFF>(n);
 }
 
 // 128-bit buffer resource (base, range in bytes) held in SGPRs.  Range

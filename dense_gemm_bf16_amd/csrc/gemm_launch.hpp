@@ -20,7 +20,8 @@ namespace gemm {
 // PIPE 6: gemm_bf16_regstage_kernel (loads staged through ST register
 // buffers, two LDS slots);
 // PIPE 8 / 10: gemm_bf16_dtl_kernel (LDS-DMA straight into an ST-slot ring)
-// with 32x32x16 / 16x16x32 MFMAs;
+// with 32x32x16 / 16x16x32 MFMAs; PIPE 11 / 12: PIPE 10 with B loaded 1 / 2
+// K-steps ahead of A in 1 / 2 more B slots;
 // PIPE 9: gemm_bf16_wavek_kernel (small M: four waves split each K-step of
 // one BM x 32 block; WM = WN = 1 name the block, 256 threads run it).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int FLAGS>
@@ -35,9 +36,9 @@ hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
   } else
 #endif
-  if constexpr (PIPE == 8 || PIPE == 10) {
+  if constexpr (PIPE == 8 || PIPE == 10 || PIPE == 11 || PIPE == 12) {
     hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, BK, WM, WN, ST, SWZ, FLAGS,
-                                             PIPE == 10 ? 16 : 32>),
+                                             PIPE == 8 ? 32 : 16, PIPE >= 11 ? PIPE - 10 : 0>),
                        dim3(grid), dim3(WM * WN * 64), 0, s, a);
   } else if constexpr (PIPE == 9) {
     static_assert(WM == 1 && WN == 1, "one block per workgroup");
@@ -53,11 +54,12 @@ hipError_t launch_one(const KernelArgs& a, int grid, hipStream_t s) {
 // LDS bytes a configuration's kernel allocates.
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE>
 constexpr int lds_bytes_of() {
-  return TileCfg<BM, BN, BK, WM, WN, PIPE == 6 ? 2 : ST, SWZ>::kLdsBytes;
+  using C = TileCfg<BM, BN, BK, WM, WN, PIPE == 6 ? 2 : ST, SWZ>;
+  return C::kLdsBytes + (PIPE >= 11 ? (PIPE - 10) * C::kBBytes : 0);
 }
 
 // Kernels with a separate K % BK != 0 variant: direct-to-LDS and small M.
-constexpr bool has_partial_variant(int pipe) { return pipe == 8 || pipe == 9 || pipe == 10; }
+constexpr bool has_partial_variant(int pipe) { return pipe >= 8 && pipe <= 12; }
 
 // The (kOutF32, kSplitK, kRaggedK) combinations that occur, with the fixed
 // bits E (kF16, kPartialK).
@@ -117,7 +119,7 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   if (flags & kSplitK) flags &= ~kOutF32;  // split slices always write fp32 partials
   if (flags & kPersistent) {
     if constexpr ((OPT & kOptPersist) != 0) {
-      static_assert(PIPE == 8 || PIPE == 10, "only the direct-to-LDS kernel walks tiles");
+      static_assert(PIPE == 8 || PIPE == 10, "only the direct-to-LDS kernel without B lead walks tiles");
       if ((flags & (kF16 | kSplitK | kOutF32)) == 0)
         return launch_partial<BM, BN, BK, WM, WN, ST, SWZ, PIPE, kPersistent>(a, grid, s, flags);
     }
@@ -165,8 +167,9 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 // measurements behind the product choices compared against -- LDS-DMA
 // spread issue (PIPE 1, 3, 4), ping-pong (2, 5), register-staged (6), the
 // 32x32x16 forms of the direct-to-LDS tiles (8), the unswizzled and
-// row-mod-8 LDS layouts (x0, x1), and the direct-to-LDS tiles on 8 waves (two
-// per SIMD: 256 x 256 as 2 x 4 or 4 x 2 waves, 256 x 128 as 4 x 2).
+// row-mod-8 LDS layouts (x0, x1), the direct-to-LDS tiles on 8 waves (two
+// per SIMD: 256 x 256 as 2 x 4 or 4 x 2 waves, 256 x 128 as 4 x 2), and the
+// 256 x 128 tile with B one or two K-steps ahead of A (PIPE 11, 12).
 #ifdef GEMM_WITH_ABLATION
 #define GEMM_ABLATION_CONFIGS(X)                                  \
   X(t256x256x64_w2x2_s2_x2_p0, 256, 256, 64, 2, 2, 2, 2, 0, 0, a) \
@@ -196,7 +199,9 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   X(t256x256x64_w2x2_s2_x1_p0, 256, 256, 64, 2, 2, 2, 1, 0, 0, j) \
   X(t256x256x64_w2x4_s2_x3_p10, 256, 256, 64, 2, 4, 2, 3, 10, 0, big8)   \
   X(t256x256x64_w4x2_s2_x3_p10, 256, 256, 64, 4, 2, 2, 3, 10, 0, big8b)  \
-  X(t256x128x64_w4x2_s3_x3_p10, 256, 128, 64, 4, 2, 3, 3, 10, 0, mid8)
+  X(t256x128x64_w4x2_s3_x3_p10, 256, 128, 64, 4, 2, 3, 3, 10, 0, mid8)   \
+  X(t256x128x64_w2x2_s3_x3_p11, 256, 128, 64, 2, 2, 3, 3, 11, 0, midb1)   \
+  X(t256x128x64_w2x2_s2_x3_p12, 256, 128, 64, 2, 2, 2, 3, 12, 0, midb2)
 #else
 #define GEMM_ABLATION_CONFIGS(X)
 #endif
