@@ -321,8 +321,8 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
       const int Y = kLast ? X + S : X + S - 1;
       // fragments read during this substep: substep kk+1 of step X, or
       // substep 0 of step X+1 once it is published
-      const lds_u8* ra = kLast ? smem + slot_off(X + 1) : sa;
-      const lds_u8* rb = kLast ? smem + b_off(X + 1) : sb;
+      const lds_u8* read_a = kLast ? smem + slot_off(X + 1) : sa;
+      const lds_u8* read_b = kLast ? smem + b_off(X + 1) : sb;
       constexpr int rkk = kLast ? 0 : kk + 1;
       const bool reads = !kLast || V <= 1 || X + 1 < n_iter;
       // MFMAs of this substep that run before the barrier (kLast only)
@@ -375,7 +375,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
                 constexpr int at = r < FM ? pos_a(r) : pos_b(r - FM);
                 if constexpr ((at < NM - 1 ? at : NM - 1) == j) {
                   if (reads)
-                    read_frag_one<Cfg, SWZ, r>(ra, rb, rkk, wm, wn, lane, fa[0],
+                    read_frag_one<Cfg, SWZ, r>(read_a, read_b, rkk, wm, wn, lane, fa[0],
                                                fb[nxt]);
                   __builtin_amdgcn_sched_barrier(0);
                 }
@@ -401,7 +401,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
               if constexpr (rn > rb) {
                 if (reads)
                   read_frag_one<Cfg, SWZ, frag_need_order<Cfg>(rb)>(
-                      ra, rb, rkk, wm, wn, lane, fa[na], fb[nxt]);
+                      read_a, read_b, rkk, wm, wn, lane, fa[na], fb[nxt]);
               } else {
                 dma_one(Y, grp * G + (p - rb));
               }
