@@ -67,7 +67,9 @@ def candidates(M: int, N: int, K: int, tiles: list[str], cus: int = 256) -> list
                 continue
             if s > 1 and n_tiles >= cus:
                 continue  # the tiles alone fill the chip
-            for g in (4, 8):
+            # GROUP_M orders tile rows; with one row of tiles every value
+            # gives the same launch, so time only one
+            for g in ((4, 8) if -(-M // bm) > 1 else (4,)):
                 for r in (0, 1):
                     name = f"{tile}_k{s}_g{g}" + (f"_r{r}" if r else "")
                     out.append(name)

@@ -97,3 +97,14 @@ def test_read_table_round_trip(tmp_path):
     write_table(rows, str(out), "note")
     assert read_table(str(out)) == {(M, N, K): p for M, N, K, p in rows}
     assert read_table(str(tmp_path / "missing.inc")) == {}
+
+
+def test_one_tile_row_times_one_group_size():
+    """GROUP_M orders rows of tiles; when M fits one tile row every value
+    gives the same launch, so only one is a candidate."""
+    from dense_gemm_bf16_amd.tune import candidates
+
+    c = candidates(256, 8192, 8192, ["t256x128x64_w2x2_s3_x3_p10"])
+    assert c and all("_g4" in p for p in c)
+    c = candidates(1024, 8192, 8192, ["t256x128x64_w2x2_s3_x3_p10"])
+    assert any("_g8" in p for p in c)
