@@ -229,7 +229,9 @@ def summarize_clocks(samples):
 
 def time_workload(g, torch, np, w, args, stream, clocks, config=None):
     """Time one workload as the module docstring describes.  Returns a dict of
-    results (plus the host arrays, for the CPU baseline)."""
+    results (plus the host arrays, for the CPU baseline).  With --context the
+    vendor library (torch.matmul) is timed the same way on the same tensors,
+    after the library, under the key "vendor"."""
     M, N, K = w.M, w.N, w.K
     half = args.dtype == "f16"
     A, B = w.make(fmt=args.dtype)
@@ -252,15 +254,39 @@ def time_workload(g, torch, np, w, args, stream, clocks, config=None):
     def step(i):
         entry(config, M, N, K, dA, K, dBs[i % sets], K, dC, N, False, stream)
 
+    res = {"M": M, "N": N, "K": K, "plan": plan, "bound": bound}
+    res.update(_measure(torch, step, flops, nbytes, bound, args, stream, clocks))
+    res["b_sets"] = sets
+    res["b_read"] = "cold" if sets > 1 else "hot"
+    if args.context:
+        tdt = torch.float16 if half else torch.bfloat16
+        a, c = dA.view(tdt), dC.view(tdt)
+        bts = [d.view(tdt).t() for d in dBs]
+
+        def vendor_step(i):
+            torch.matmul(a, bts[i % sets], out=c)
+
+        v = _measure(torch, vendor_step, flops, nbytes, bound, args, stream, clocks)
+        v["library"] = "torch.matmul"
+        v["us_ratio_library_over_vendor"] = round(res["us"] / v["us"], 4)
+        res["vendor"] = v
+    return res, (A, B, dA, dBs, dC, stream)
+
+
+def _measure(torch, step, flops, nbytes, bound, args, stream, clocks):
+    """Clock ramp, warm-up, the timed launches, the repeats and the clocks
+    of the module docstring, for one launch function."""
+
     def timed(n):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        e0.record(stream)
-        for i in range(n):
-            step(i)
-        e1.record(stream)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(n):
+                step(i)
+            e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3, time.perf_counter() - w0  # us per launch
 
@@ -280,7 +306,7 @@ def time_workload(g, torch, np, w, args, stream, clocks, config=None):
     us, wall = timed(args.steps)
     reps = [timed(args.steps)[0] for _ in range(args.repeats)]
 
-    # clocks: the same GEMM keeps running, untimed, until the GPU metrics
+    # clocks: the same launches keep running, untimed, until the GPU metrics
     # have been refreshed after the timed region began (at most --clock-s)
     samples = []
     if clocks is not None and t_begin is not None:
@@ -300,13 +326,11 @@ def time_workload(g, torch, np, w, args, stream, clocks, config=None):
     t = us * 1e-6
     tflops = flops / t / 1e12
     gbps = nbytes / t / 1e9
-    res = {
-        "M": M, "N": N, "K": K, "plan": plan, "bound": bound,
+    return {
         "us": round(us, 2), "tflops": round(tflops, 1), "tbps": round(gbps / 1e3, 3),
         "pct_mfma_peak": round(100 * tflops / PEAK_TFLOPS, 2),
         "pct_hbm_bw": round(100 * gbps / PEAK_GBPS, 2),
         "frac": round((tflops / PEAK_TFLOPS) if bound == "mfma" else (gbps / PEAK_GBPS), 4),
-        "b_sets": sets, "b_read": "cold" if sets > 1 else "hot",
         "repeats_us": {"n": len(reps), "min": round(min(reps), 2),
                        "median": round(statistics.median(reps), 2),
                        "max": round(max(reps), 2)} if reps else None,
@@ -314,7 +338,6 @@ def time_workload(g, torch, np, w, args, stream, clocks, config=None):
         "clocks": summarize_clocks(samples),
         "wall_s_timed": round(wall, 4),
     }
-    return res, (A, B, dA, dBs, dC, stream)
 
 
 def main() -> int:
@@ -342,7 +365,8 @@ def main() -> int:
                     help="target length of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--context", action="store_true",
-                    help="also time torch.matmul on the same tensors (context only)")
+                    help="also time the vendor library (torch.matmul) on the same tensors, "
+                         "the same way, for every timed shape (context only; never the value)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (for counter "
                          "calibration) and exit")
@@ -437,20 +461,7 @@ def main() -> int:
         out["workloads"] = wl
 
     if args.context:
-        tdt = torch.float16 if half else torch.bfloat16
-        a = torch.from_numpy(A.view(np.int16)).cuda().view(tdt)
-        b = torch.from_numpy(B.view(np.int16)).cuda().view(tdt)
-        with torch.cuda.stream(stream):
-            for _ in range(5):
-                torch.matmul(a, b.t())
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                torch.matmul(a, b.t())
-            e1.record(stream)
-        torch.cuda.synchronize()
-        out["context"] = {"torch_matmul_tflops": round(flops / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12, 2)}
+        out["context"] = {"vendor": head["vendor"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds, args.dtype)
     print(json.dumps(out), flush=True)
