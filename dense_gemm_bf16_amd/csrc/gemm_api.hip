@@ -180,7 +180,9 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
   if (p->k_rot > 0 && n > 0 && n < (int)sizeof p->name)
     n += snprintf(p->name + n, sizeof p->name - n, "_r%d", p->k_rot);
   if (p->persist > 0 && n > 0 && n < (int)sizeof p->name)
-    snprintf(p->name + n, sizeof p->name - n, "_P%d", p->persist);
+    n += snprintf(p->name + n, sizeof p->name - n, "_P%d", p->persist);
+  if (p->stream_b > 0 && n > 0 && n < (int)sizeof p->name)
+    snprintf(p->name + n, sizeof p->name - n, "_n1");
 }
 
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out);
@@ -208,6 +210,10 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
                  : find_tile_config(M <= 32 ? kSkinny32 : kSkinny64);
     p.splits = choose_splits(tiles_of(p.tile, M, N), (K + p.tile->bk - 1) / p.tile->bk);
     p.k_rot = 1;
+    // one row of tiles: no other workgroup reads a workgroup's B, so its
+    // loads are non-temporal (M = 1 and 17 at 8192 x 8192: 25.7 -> 21.9 and
+    // 24.7 -> 21.7 us)
+    p.stream_b = (M + p.tile->bm - 1) / p.tile->bm == 1 && p.tile->stream ? 1 : 0;
   } else if (big_tiles >= kCUs - kCUs / 8) {
     p.tile = big;
     p.splits = 1;
@@ -234,14 +240,15 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
   return p;
 }
 
-// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>]" where tile is a
-// table name (_P: a persistent grid of that many workgroups walking the
-// tiles; only for tiles built with it, bf16 operands, and never split).
+// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>][_n<0|1>]" where
+// tile is a table name (_P: a persistent grid of that many workgroups
+// walking the tiles; only for tiles built with it, bf16 operands, and never
+// split.  _n1: non-temporal B loads, only for tiles built with them).
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out) {
   char buf[64];
   if (strlen(name) >= sizeof buf) return false;
   strcpy(buf, name);
-  int splits = 1, group = 4, rot = 0, persist = 0;
+  int splits = 1, group = 4, rot = 0, persist = 0, stream = 0;
   for (;;) {
     char* u = strrchr(buf, '_');
     if (!u) break;
@@ -258,7 +265,9 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
     } else if (u[1] == 'P' && sscanf(u + 2, "%d", &v) == 1 && v >= 1) {
       persist = v;
       *u = 0;
-
+    } else if (u[1] == 'n' && sscanf(u + 2, "%d", &v) == 1 && (v == 0 || v == 1)) {
+      stream = v;
+      *u = 0;
     } else {
       break;
     }
@@ -266,11 +275,13 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
   const TileConfig* t = find_tile_config(buf);
   if (!t) return false;
   if (persist > 0 && (!t->persist || splits > 1)) return false;
+  if (stream && !t->stream) return false;
   out->tile = t;
   out->splits = splits;
   out->group_m = group;
   out->k_rot = rot;
   out->persist = persist;
+  out->stream_b = stream;
   finish_plan(out, M, N, K);
   return true;
 }
@@ -337,6 +348,9 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   if (K % t.bk != 0) flags |= kPartialK;
   // (fp32 output: the ordinary kernel, whose per-tile K order is the same)
   if (p.persist > 0 && !out_f32) flags |= kPersistent;
+  // (where no kernel with non-temporal B loads is built for the other
+  // flags, the launcher runs the ordinary one: same sums, same results)
+  if (p.stream_b > 0) flags |= kStreamB;
   void* ws = nullptr;
   if (p.splits > 1) {
     const size_t need = workspace_bytes(p, M, N);

@@ -10,10 +10,10 @@ const TileConfig* tile_configs() {
 #define GEMM_TABLE_ROW(NAME, BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT, TU)                 \
   {#NAME, BM, BN, BK, PIPE == 9 ? 256 : WM * WN * 64,                                  \
    lds_bytes_of<BM, BN, BK, WM, WN, ST, SWZ, PIPE>(),                                     \
-   (OPT & kOptF16) != 0, (OPT & kOptPersist) != 0,                                        \
+   (OPT & kOptF16) != 0, (OPT & kOptPersist) != 0, (OPT & kOptStream) != 0,              \
    &launch_cfg<BM, BN, BK, WM, WN, ST, SWZ, PIPE, OPT>},
   static const TileConfig table[] = {
-      GEMM_TILE_CONFIGS(GEMM_TABLE_ROW){nullptr, 0, 0, 0, 0, 0, false, false, nullptr}};
+      GEMM_TILE_CONFIGS(GEMM_TABLE_ROW){nullptr, 0, 0, 0, 0, 0, false, false, false, nullptr}};
 #undef GEMM_TABLE_ROW
   return table;
 }

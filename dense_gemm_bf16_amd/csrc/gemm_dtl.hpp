@@ -81,6 +81,7 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
   constexpr bool kHalf = (FLAGS & kF16) != 0;
   constexpr bool kSplit = (FLAGS & kSplitK) != 0;
   constexpr bool kRagged = (FLAGS & kRaggedK) != 0;    // K % 8 != 0
+  constexpr bool kStream = (FLAGS & kStreamB) != 0;    // B loads non-temporal
   constexpr bool kPartial = (FLAGS & kPartialK) != 0;  // K % BK != 0
   static_assert(!kRagged || kPartial, "K % 8 != 0 implies K % BK != 0");
   static_assert(SUB % 2 == 0, "fragment buffers alternate per substep, also across steps");
@@ -187,9 +188,17 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
     const int YS = is_a ? Y : Y + DL;  // the K-step this load belongs to
     const uint32_t dst = smem_addr + (is_a ? slot_off(Y) : b_off(YS)) + lds_off(i);
     const u32x4& rs = is_a ? rsrc_a : rsrc_b;
+    // (i is a constant wherever this is called, so is_a picks the form at
+    // compile time)
+    auto load = [&](uint32_t v, uint32_t so) __attribute__((always_inline)) {
+      if (is_a)
+        dma16(rs, dst, v, so);
+      else
+        dma16<kStream>(rs, dst, v, so);
+    };
     if constexpr (DL > 0) {
       if (YS >= n_iter) {  // past the end: keep the stage's load count
-        dma16(rs, dst, kOOB, 0u);
+        load(kOOB, 0u);
         return;
       }
     }
@@ -198,12 +207,11 @@ gemm_bf16_dtl_kernel(KernelArgs a) {
       if (kt >= full_tiles) {
         const int k0 = kt * BK;
         const int c = chunk2[(i < LA ? i : i - LA) & 1];
-        const uint32_t v = (k0 + c * 8 < a.K) ? voff[i] + (uint32_t)(k0 * 2) : kOOB;
-        dma16(rs, dst, v, 0u);
+        load((k0 + c * 8 < a.K) ? voff[i] + (uint32_t)(k0 * 2) : kOOB, 0u);
         return;
       }
     }
-    dma16(rs, dst, voff[i], (uint32_t)(kt * BK * 2));
+    load(voff[i], (uint32_t)(kt * BK * 2));
   };
 
   // Trim the chunk that straddles K in this thread's part of step Y's A and

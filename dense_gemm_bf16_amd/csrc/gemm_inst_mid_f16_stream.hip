@@ -1,0 +1,6 @@
+// Kernel instantiations of the 256 x 128 direct-to-LDS tile ("mid" in GEMM_TILE_CONFIGS):
+// fp16 operands, whole K-steps, non-temporal B loads.
+#define GEMM_SPLIT_PARAMS GEMM_MID_PARAMS
+#define GEMM_SPLIT_STREAM
+#define GEMM_SPLIT_OWN 72
+#include "gemm_inst_split.hpp"

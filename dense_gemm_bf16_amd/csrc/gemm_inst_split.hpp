@@ -16,7 +16,10 @@
 // or 28 (fp16), as they would otherwise make the K-tail files the longest
 // of the build.  With GEMM_SPLIT_PERSIST defined (rows built with
 // kOptPersist), the persistent-grid groups (kPersistent, with and without
-// kPartialK) are instantiated by the files with GEMM_SPLIT_OWN 32 and 48.
+// kPartialK) are instantiated by the files with GEMM_SPLIT_OWN 32 and 48;
+// with GEMM_SPLIT_STREAM defined (rows built with kOptStream), the kernels
+// with non-temporal B loads by the files with GEMM_SPLIT_OWN 64 (bf16) and
+// 72 (fp16).
 #pragma once
 
 #include "gemm_launch.hpp"
@@ -30,6 +33,10 @@
   template hipError_t launch_variant<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E>( \
       const KernelArgs&, int, hipStream_t, int);
 #define GEMM_SPLIT_VARIANT(E) GEMM_SPLIT_EXPAND(GEMM_SPLIT_VARIANT_, E, GEMM_SPLIT_PARAMS)
+#define GEMM_SPLIT_STREAM_(E, BM, BN, BK, WM, WN, ST, SWZ, PIPE)          \
+  template hipError_t launch_stream<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E>( \
+      const KernelArgs&, int, hipStream_t, int);
+#define GEMM_SPLIT_STREAM_GROUP(E) GEMM_SPLIT_EXPAND(GEMM_SPLIT_STREAM_, E, GEMM_SPLIT_PARAMS)
 #define GEMM_SPLIT_ONE_(F, BM, BN, BK, WM, WN, ST, SWZ, PIPE)          \
   template hipError_t launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, F>( \
       const KernelArgs&, int, hipStream_t);
@@ -44,6 +51,19 @@ namespace gemm {
 static_assert(kF16 == 8 && kPartialK == 16 && kRaggedK == 4,
               "GEMM_SPLIT_OWN numbers the groups by these bits");
 static_assert(kPersistent == 32, "GEMM_SPLIT_OWN 32 and 48 name the persistent groups");
+#ifdef GEMM_SPLIT_STREAM
+static_assert(kStreamB == 64, "GEMM_SPLIT_OWN 64 and 72 name the stream-B groups");
+#if GEMM_SPLIT_OWN == 64
+GEMM_SPLIT_STREAM_GROUP(0)
+#else
+extern GEMM_SPLIT_STREAM_GROUP(0)
+#endif
+#if GEMM_SPLIT_OWN == 72
+GEMM_SPLIT_STREAM_GROUP(8)
+#else
+extern GEMM_SPLIT_STREAM_GROUP(8)
+#endif
+#endif
 #ifdef GEMM_SPLIT_PERSIST
 #if GEMM_SPLIT_OWN == 32
 GEMM_SPLIT_VARIANT(32)

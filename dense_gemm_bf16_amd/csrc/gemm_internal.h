@@ -11,8 +11,8 @@
 namespace gemm {
 
 // One compiled tile configuration.  `launch` takes the variant flags
-// (kOutF32 | kSplitK | kRaggedK | kF16) and enqueues the matching kernel;
-// kF16 only where `f16` is set.
+// (kOutF32 | kSplitK | kRaggedK | kF16 | kPartialK | kPersistent | kStreamB)
+// and enqueues the matching kernel; kF16 only where `f16` is set.
 struct TileConfig {
   const char* name;  // e.g. "t256x256x64_w2x2_s2_x2"
   int bm, bn;        // output tile
@@ -21,6 +21,7 @@ struct TileConfig {
   int lds_bytes;     // static LDS per workgroup
   bool f16;          // also built for fp16 operands
   bool persist;      // also built for a persistent grid (bf16 operands)
+  bool stream;       // also built with non-temporal B loads (kStreamB)
   hipError_t (*launch)(const KernelArgs&, int grid, hipStream_t, int flags);
 };
 
@@ -36,6 +37,7 @@ struct Plan {
   int group_m;
   int k_rot;    // K-step rotation stride per tile, 0 = none
   int persist;  // persistent grid of this many workgroups (a multiple of 8), 0 = none
+  int stream_b; // 1: B loads non-temporal (where the tile is built with it)
   char name[64];
 };
 

@@ -112,11 +112,36 @@ hipError_t launch_partial(const KernelArgs& a, int grid, hipStream_t s, int flag
 enum : int {
   kOptF16 = 1,      // the fp16-operand kernels
   kOptPersist = 2,  // the persistent-grid kernels, bf16 operands (direct-to-LDS only)
+  kOptStream = 4,   // kernels with non-temporal B loads (kStreamB): whole K-steps,
+                    // 16-bit output, plain and split
 };
+
+// The kStreamB kernels of operand type E (0 or kF16): 16-bit output or split
+// K (flags & 7 is 0 or kSplitK; the caller has checked).
+template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int E>
+hipError_t launch_stream(const KernelArgs& a, int grid, hipStream_t s, int flags) {
+  if (flags & kSplitK)
+    return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | kStreamB | kSplitK>(a, grid, s);
+  return launch_one<BM, BN, BK, WM, WN, ST, SWZ, PIPE, E | kStreamB>(a, grid, s);
+}
 
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SWZ, int PIPE, int OPT>
 hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
   if (flags & kSplitK) flags &= ~kOutF32;  // split slices always write fp32 partials
+  if (flags & kStreamB) {
+    flags &= ~kStreamB;
+    // Where no such kernel is built (fp32 output, a K that is not a whole
+    // number of K-steps, a persistent grid, or a row without kOptStream)
+    // the ordinary kernel runs: the loads' cache policy changes no result.
+    if constexpr ((OPT & kOptStream) != 0) {
+      if ((flags & (kOutF32 | kRaggedK | kPartialK | kPersistent)) == 0) {
+        if ((flags & kF16) == 0)
+          return launch_stream<BM, BN, BK, WM, WN, ST, SWZ, PIPE, 0>(a, grid, s, flags);
+        if constexpr ((OPT & kOptF16) != 0)
+          return launch_stream<BM, BN, BK, WM, WN, ST, SWZ, PIPE, kF16>(a, grid, s, flags);
+      }
+    }
+  }
   if (flags & kPersistent) {
     if constexpr ((OPT & kOptPersist) != 0) {
       static_assert(PIPE == 8 || PIPE == 10, "only the direct-to-LDS kernel without B lead walks tiles");
@@ -136,8 +161,9 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 
 // Built configurations, one row each:
 //   X(name, BM, BN, BK, WAVES_M, WAVES_N, STAGES, SWZ, PIPE, OPT, TU)
-// where OPT is a mask of kOptF16 (also build the row for fp16 operands) and
-// kOptPersist (also build its persistent-grid kernels), and TU names the
+// where OPT is a mask of kOptF16 (also build the row for fp16 operands),
+// kOptPersist (also build its persistent-grid kernels) and kOptStream (also
+// build its kernels with non-temporal B loads), and TU names the
 // gemm_inst_<TU>.hip file that instantiates it.  A row whose parameters
 // are also needed elsewhere (the files that split its kernel variants over
 // several translation units) takes them from a GEMM_*_PARAMS macro, through
@@ -155,12 +181,12 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 #define GEMM_MID_PARAMS 256, 128, 64, 2, 2, 3, 3, 10
 #define GEMM_PRODUCT_CONFIGS(X)                                        \
   GEMM_ROW(X, t256x256x64_w2x2_s2_x3_p10, GEMM_BIG_PARAMS, 3, big)     \
-  GEMM_ROW(X, t256x128x64_w2x2_s3_x3_p10, GEMM_MID_PARAMS, 1, mid)     \
+  GEMM_ROW(X, t256x128x64_w2x2_s3_x3_p10, GEMM_MID_PARAMS, 5, mid)     \
   X(t128x128x64_w2x2_s4_x3_p10, 128, 128, 64, 2, 2, 4, 3, 10, 1, mid128) \
-  X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 1, smallm)     \
-  X(t64x32x64_w1x1_s6_x2_p9, 64, 32, 64, 1, 1, 6, 2, 9, 1, smallm)     \
-  X(t64x128x64_w1x4_s6_x2_p0, 64, 128, 64, 1, 4, 6, 2, 0, 1, skinny)   \
-  X(t32x128x64_w1x4_s6_x2_p0, 32, 128, 64, 1, 4, 6, 2, 0, 1, skinny)
+  X(t32x32x64_w1x1_s8_x2_p9, 32, 32, 64, 1, 1, 8, 2, 9, 5, smallm)     \
+  X(t64x32x64_w1x1_s6_x2_p9, 64, 32, 64, 1, 1, 6, 2, 9, 5, smallm)     \
+  X(t64x128x64_w1x4_s6_x2_p0, 64, 128, 64, 1, 4, 6, 2, 0, 5, skinny)   \
+  X(t32x128x64_w1x4_s6_x2_p0, 32, 128, 64, 1, 4, 6, 2, 0, 5, skinny)
 
 // The ablation set (built only with GEMM_WITH_ABLATION, by
 // build(ablation=True)): the other kernel families and layouts that the

@@ -37,6 +37,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_bf16
   constexpr bool kHalf = (FLAGS & kF16) != 0;
   constexpr bool kSplit = (FLAGS & kSplitK) != 0;
   constexpr bool kRagged = (FLAGS & kRaggedK) != 0;
+  constexpr bool kStream = (FLAGS & kStreamB) != 0;  // B loads non-temporal
   constexpr bool kPartial = (FLAGS & kPartialK) != 0;
   static_assert(BN == 32 && BK == 64, "32 columns, four 16-wide substeps per step");
   static_assert(Cfg::kSub == 4, "one substep per wave");
@@ -109,13 +110,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void gemm_bf16
       const uint32_t dst =
           slot + (uint32_t)((is_a ? 0 : Cfg::kABytes) + ((is_a ? i : i - LA) * T + wave * 64) * 16);
       const u32x4& rs = is_a ? rsrc_a : rsrc_b;
+      uint32_t v = voff[i], so = (uint32_t)(kt * BK * 2);
       if (kPartial && kt >= full_tiles) {
         const int k0 = kt * BK;
-        const uint32_t v = (k0 + chunk[i] * 8 < a.K) ? voff[i] + (uint32_t)(k0 * 2) : kOOB;
-        dma16(rs, dst, v, 0u);
-      } else {
-        dma16(rs, dst, voff[i], (uint32_t)(kt * BK * 2));
+        v = (k0 + chunk[i] * 8 < a.K) ? voff[i] + (uint32_t)(k0 * 2) : kOOB;
+        so = 0u;
       }
+      if (is_a)
+        dma16(rs, dst, v, so);
+      else
+        dma16<kStream>(rs, dst, v, so);
     }
   };
 

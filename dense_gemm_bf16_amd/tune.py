@@ -10,7 +10,8 @@ For each shape the sweep
 1. enumerates candidates (every tile built for the operand type, except
    the LDS-layout ablation tiles; split counts that keep at least four
    K-steps per slice and at most ~4 workgroups per CU; GROUP_M 4 and 8;
-   rotation off and on),
+   rotation off and on; with one row of tiles, non-temporal B loads off and
+   on where the tile is built with them),
 2. times every candidate briefly (HIP events on one stream, after a warm-up
    long enough for the clock to settle; memory-bound shapes cycle through
    copies of B larger than the 256 MB Infinity Cache, as ``bench.py`` does),
@@ -50,8 +51,11 @@ def parse_tile(name: str):
     return int(dims[0]), int(dims[1]), int(dims[2])
 
 
-def candidates(M: int, N: int, K: int, tiles: list[str], cus: int = 256) -> list[str]:
-    """Plan names worth timing for one shape (no GPU needed)."""
+def candidates(M: int, N: int, K: int, tiles: list[str], cus: int = 256,
+               stream_tiles: frozenset = frozenset()) -> list[str]:
+    """Plan names worth timing for one shape (no GPU needed).  For the tiles
+    in ``stream_tiles`` (built with non-temporal B loads) and a single row of
+    tiles, every plan is also tried with "_n1"."""
     out = []
     for tile in tiles:
         if any(a in tile for a in ABLATION_TILES):
@@ -69,11 +73,29 @@ def candidates(M: int, N: int, K: int, tiles: list[str], cus: int = 256) -> list
                 continue  # the tiles alone fill the chip
             # GROUP_M orders tile rows; with one row of tiles every value
             # gives the same launch, so time only one
-            for g in ((4, 8) if -(-M // bm) > 1 else (4,)):
+            one_row = -(-M // bm) == 1
+            for g in ((4, 8) if not one_row else (4,)):
                 for r in (0, 1):
                     name = f"{tile}_k{s}_g{g}" + (f"_r{r}" if r else "")
                     out.append(name)
+                    if one_row and tile in stream_tiles:
+                        out.append(name + "_n1")
     return out
+
+
+def stream_tiles(g, tiles: list[str]) -> frozenset:
+    """The tiles whose plans accept "_n1" (asked of the library with M = 0,
+    so nothing is launched)."""
+    import ctypes
+
+    fake = ctypes.c_void_p(0x10000)
+    ok = set()
+    for t in tiles:
+        rc = g._lib.gemm_bf16_ex((t + "_k1_g4_n1").encode(), 0, 64, 64, fake, 64, fake, 64,
+                                 fake, 64, 0, None)
+        if rc == g.GEMM_OK:
+            ok.add(t)
+    return frozenset(ok)
 
 
 def _time_plans(lib_call, plans, n, sets, reps=1):
@@ -106,7 +128,7 @@ def tune_shape(M: int, N: int, K: int, half: bool = False, keep: int = 6,
     import dense_gemm_bf16_amd as g
 
     tiles = g.f16_config_names() if half else g.config_names()
-    plans = candidates(M, N, K, tiles)
+    plans = candidates(M, N, K, tiles, stream_tiles=stream_tiles(g, tiles))
     auto = g.config_name(M, N, K)
     if auto not in plans:
         plans.append(auto)

@@ -115,8 +115,17 @@ int gemm_bf16_ex(const char* config,
  * same for both operand types) would choose for this shape, e.g.
  * "t256x256x64_w2x2_s2_x3_p10_k1_g4": tile BM x BN x BK, waves, ring stages,
  * LDS swizzle, load schedule, then K splits and GROUP_M (and "_r<n>", the
- * K-step rotation, when on).  Per-thread static storage, valid until the
- * thread's next call; never NULL.
+ * K-step rotation, when on, and "_n1" when B is loaded non-temporally).
+ * Per-thread static storage, valid until the thread's next call; never NULL.
+ *
+ * "_n1" (accepted by gemm_bf16_ex / gemm_f16_ex on the tiles built for it:
+ * the 256 x 128 direct-to-LDS tile and the M <= 64 tiles) marks B's loads
+ * non-temporal, so the L2 does not keep B for reuse.  It is meant for one
+ * row of tiles (M no larger than the tile's BM), where no other workgroup
+ * reads the same B; it changes only the cache policy, so results are the
+ * same bits as without it.  Calls with fp32 output, or a K that is not a
+ * whole number of the tile's K-steps, run the ordinary kernel.  "_n0" is
+ * accepted and means the default (no suffix).
  *
  * gemm_bf16_ex also accepts a "_P<n>" suffix on the tile built for it
  * (t256x256x64_w2x2_s2_x3_p10): a persistent grid of n workgroups (rounded

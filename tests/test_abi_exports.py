@@ -139,6 +139,33 @@ def test_persistent_plan_names_on_the_host(lib):
     assert rc(big + "_k1_g4_P256", half=True) == lib.GEMM_ERR_UNSUPPORTED
 
 
+def test_stream_b_plan_names_on_the_host(lib):
+    """Plan names with non-temporal B loads (_n1): accepted for the tiles
+    built with them (M = 0, so nothing is launched), also with fp16 operands,
+    refused on the others; _n0 is the default; the automatic plan has it for
+    one row of small-M tiles."""
+    so = lib._lib
+    fake = ctypes.c_void_p(0x10000)
+
+    def rc(name, half=False):
+        fn = so.gemm_f16_ex if half else so.gemm_bf16_ex
+        return fn(name.encode(), 0, 8192, 8192, fake, 8192, fake, 8192, fake, 8192, 0, None)
+
+    for tile in ("t256x128x64_w2x2_s3_x3_p10", "t32x32x64_w1x1_s8_x2_p9",
+                 "t64x32x64_w1x1_s6_x2_p9", "t64x128x64_w1x4_s6_x2_p0",
+                 "t32x128x64_w1x4_s6_x2_p0"):
+        assert rc(tile + "_k4_g4_r1_n1") == lib.GEMM_OK, tile
+        assert rc(tile + "_k1_g4_n1", half=True) == lib.GEMM_OK, tile
+        assert rc(tile + "_k1_g4_n0") == lib.GEMM_OK, tile
+        assert rc(tile + "_k1_g4_n2") == lib.GEMM_ERR_UNSUPPORTED, tile
+    for tile in ("t256x256x64_w2x2_s2_x3_p10", "t128x128x64_w2x2_s4_x3_p10"):
+        assert rc(tile + "_k1_g4_n1") == lib.GEMM_ERR_UNSUPPORTED, tile
+        assert rc(tile + "_k1_g4_n0") == lib.GEMM_OK, tile
+    assert lib.config_name(1, 8192, 8192).endswith("_n1")
+    assert lib.config_name(17, 8192, 8192).endswith("_n1")
+    assert not lib.config_name(4096, 4096, 4096).endswith("_n1")
+
+
 def test_config_names(lib):
     names = lib.config_names()
     assert len(names) == len(set(names)) >= 2
@@ -149,7 +176,7 @@ def test_config_names(lib):
 
     for w in WORKLOADS.values():
         chosen = lib.config_name(w.M, w.N, w.K)
-        m = re.match(r"^(.*)_k(\d+)_g(\d+)(_r\d+)?$", chosen)
+        m = re.match(r"^(.*)_k(\d+)_g(\d+)(_r\d+)?(_n1)?$", chosen)
         assert m and m.group(1) in names, chosen
         S = int(m.group(2))
         ws = lib.workspace_size(w.M, w.N, w.K)
@@ -169,7 +196,7 @@ def test_f16_configs(lib):
     shapes = [(w.M, w.N, w.K) for w in WORKLOADS.values()]
     shapes += [(1, 16, 8), (64, 64, 64), (65, 4096, 4096), (224, 8192, 1024), (8192, 256, 64)]
     for M, N, K in shapes:
-        tile = re.match(r"^(.*)_k\d+_g\d+(_r\d+)?$", lib.config_name(M, N, K)).group(1)
+        tile = re.match(r"^(.*)_k\d+_g\d+(_r\d+)?(_n1)?$", lib.config_name(M, N, K)).group(1)
         assert tile in f16, (M, N, K, tile)
     assert lib.f16_config_at(len(f16)) is None and lib.f16_config_at(-1) is None
 

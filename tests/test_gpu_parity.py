@@ -393,3 +393,53 @@ def test_persistent_plan_k_zero():
     g.gemm_bf16_ex(BIG + "_k1_g4_P8", 300, 600, 0, dummy, 8, dummy, 8, C, 600)
     torch.cuda.synchronize()
     assert not C.cpu().numpy().any()
+
+
+# ------------------------------------------------------ non-temporal B loads
+
+# The configurations built with non-temporal B loads ("_n1"), by tile height.
+STREAM_TILES = {
+    "t256x128x64_w2x2_s3_x3_p10": 256,
+    "t32x32x64_w1x1_s8_x2_p9": 32,
+    "t64x32x64_w1x1_s6_x2_p9": 64,
+    "t64x128x64_w1x4_s6_x2_p0": 64,
+    "t32x128x64_w1x4_s6_x2_p0": 32,
+}
+
+
+@pytest.mark.parametrize("tile", sorted(STREAM_TILES))
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_stream_b_plans_bit_exact(tile, fmt):
+    """_n1 changes only the cache policy of B's loads: on integer inputs with
+    one row of tiles (ragged M and N), plain and split K, the result is
+    bit-exact and the same bits as the plan without _n1; with fp32 output and
+    with K % 64 != 0 (no such kernel: the ordinary one runs) it is exact
+    too."""
+    bm = STREAM_TILES[tile]
+    M, N = bm - 3, 1000
+    o = _oracle()
+    for K, plans in ((1024, ("_k1_g4_n1", "_k3_g4_r1_n1")), (1000, ("_k2_g4_n1",))):
+        A = int_bf16(M, K, seed=1400 + bm + K, fmt=fmt)
+        B = int_bf16(N, K, seed=1401 + bm + K, fmt=fmt)
+        ref16, ref64 = o.gemm(A, B, fmt=fmt)
+        for plan in plans:
+            name = tile + plan
+            got = run_gemm(A, B, config=name, fmt=fmt)
+            rep = check_bf16(got, ref16, None, K, exact=True, fmt=fmt)
+            print(fmt, K, name, rep, flush=True)
+            assert rep["ok"], (name, rep)
+            plain = run_gemm(A, B, config=name[: -len("_n1")], fmt=fmt)
+            assert np.array_equal(got, plain), name
+            got32 = run_gemm(A, B, config=name, out_f32=True, fmt=fmt)
+            assert check_f32(got32, ref64, K, exact=True)["ok"], name
+
+
+def test_stream_b_with_several_tile_rows_is_still_exact():
+    """_n1 where rows of tiles share B (M = 600 on the 256-row tile): slower,
+    never wrong."""
+    M, N, K = 600, 700, 512
+    A = int_bf16(M, K, seed=1450)
+    B = int_bf16(N, K, seed=1451)
+    ref16, _ = _oracle().gemm(A, B)
+    got = run_gemm(A, B, config="t256x128x64_w2x2_s3_x3_p10_k2_g4_n1")
+    assert check_bf16(got, ref16, None, K, exact=True)["ok"]

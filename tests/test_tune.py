@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TABLE = os.path.join(ROOT, "dense_gemm_bf16_amd", "csrc", "gemm_tuned.inc")
-PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d+)_k(\d+)_g(\d+)(_r\d+)?$")
+PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d+)_k(\d+)_g(\d+)(_r\d+)?(_n1)?$")
 ROW = re.compile(r'^\{(\d+), (\d+), (\d+), "([^"]+)"\},$')
 
 
@@ -47,6 +47,24 @@ def test_candidates_are_valid_plans(lib):
             assert all(PLAN.match(p).group(2) == "1" for p in c)
 
 
+def test_stream_candidates_only_for_one_row_of_tiles(lib):
+    """_n1 candidates exist exactly for the tiles that accept it and shapes
+    with a single row of those tiles."""
+    from dense_gemm_bf16_amd.tune import candidates, parse_tile, stream_tiles
+
+    tiles = lib.config_names()
+    st = stream_tiles(lib, tiles)
+    assert "t256x128x64_w2x2_s3_x3_p10" in st and "t32x32x64_w1x1_s8_x2_p9" in st
+    assert "t256x256x64_w2x2_s2_x3_p10" not in st
+    for M, N, K in [(256, 8192, 8192), (1, 8192, 8192), (600, 8192, 8192)]:
+        for p in candidates(M, N, K, tiles, stream_tiles=st):
+            if p.endswith("_n1"):
+                tile = PLAN.match(p).group(1)
+                assert tile in st and -(-M // parse_tile(tile)[0]) == 1, p
+    assert any(p.endswith("_n1") for p in candidates(256, 8192, 8192, tiles, stream_tiles=st))
+    assert not any(p.endswith("_n1") for p in candidates(4096, 4096, 4096, tiles, stream_tiles=st))
+
+
 def test_written_table_format(tmp_path):
     from dense_gemm_bf16_amd.tune import write_table
 
@@ -70,6 +88,7 @@ def test_committed_table_entries_are_used(lib):
         cm = PLAN.match(chosen)
         assert cm.group(1) == pm.group(1) and cm.group(3) == pm.group(3), (plan, chosen)
         assert (cm.group(4) or "") == (pm.group(4) or ""), (plan, chosen)
+        assert (cm.group(5) or "") == (pm.group(5) or ""), (plan, chosen)
 
 
 def test_choose_entries_keeps_still_best_table_rows():
