@@ -709,7 +709,12 @@ struct LdsStage {
   }
 };
 
-template <typename Cfg, int OUT, int LIMIT = Cfg::kLdsBytes>
+// NT stores the rows non-temporally: for C, which this kernel never reads
+// back (measured 0.7-2 % faster at 4096^3 and 8192^3, where C would
+// otherwise evict A and B panels from L2).  Split-K partials are stored
+// normally, since the reduction reads them right after (non-temporal, their
+// calls were ~1 % slower).
+template <typename Cfg, int OUT, int LIMIT = Cfg::kLdsBytes, bool NT = false>
 __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int64_t ld,
                                                const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                int m_base, int n_base, int lane) {
@@ -752,7 +757,11 @@ __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int6
       u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(buf + St::off(r, rc));
       if constexpr (St::kSwapHalves)
         if (((j * RPI) & 16) != 0) v = (u32x4){v[2], v[3], v[0], v[1]};
-      *(u32x4*)(out + (int64_t)((pass * St::kPassRows + j * RPI) * kE) * ld) = v;
+      u32x4* const dst = (u32x4*)(out + (int64_t)((pass * St::kPassRows + j * RPI) * kE) * ld);
+      if constexpr (NT)
+        __builtin_nontemporal_store(v, dst);
+      else
+        *dst = v;
     }
   }
 }
@@ -779,8 +788,8 @@ __device__ __forceinline__ void finish_tile(const KernelArgs& a, lds_u8* smem, i
       // every wave is done with the ring: loads landed, fragments read
       // (kBarrier false: the caller has made sure of it)
       if constexpr (kBarrier) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      store_tile_lds<Cfg, kOut, LIMIT>(smem + wave * St::kWaveBytes, base, ld, acc, m_base,
-                                       n_base, lane);
+      store_tile_lds<Cfg, kOut, LIMIT, !SPLIT>(smem + wave * St::kWaveBytes, base, ld, acc,
+                                               m_base, n_base, lane);
       return;
     }
   }
