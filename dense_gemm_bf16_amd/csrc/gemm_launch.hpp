@@ -1,5 +1,6 @@
 // Launcher template for one tile configuration: maps the run-time variant
-// flags (kOutF32 | kSplitK | kRaggedK | kF16) to the instantiated kernels.  Each
+// flags (kOutF32 | kSplitK | kRaggedK | kF16 | kPartialK | kPersistent |
+// kStreamB) to the instantiated kernels.  Each
 // gemm_inst_*.hip file instantiates it for its configurations, so the
 // configurations compile in parallel.
 #pragma once

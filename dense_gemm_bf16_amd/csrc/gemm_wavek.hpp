@@ -7,7 +7,9 @@
 // BK = 64 brings BM + 32 rows of 128 bytes into an S-slot LDS ring with
 // LDS-DMA loads (coalesced: 8 lanes per 128-byte row segment), and wave w
 // multiplies 16-wide substep w of that step: kFragM MFMAs of 32 x 32 x 16.
-// A deep ring (S = 8: seven steps in flight per CU) covers the HBM latency.
+// A deep ring (S = 8: seven steps in flight per CU) covers the HBM latency,
+// and with kStreamB (one row of tiles, so no other workgroup reads this B)
+// B's loads are non-temporal.
 // At the end every wave holds the partial sums of its quarter of K; they
 // meet in LDS and are added in the fixed order wave 0, 1, 2, 3, so the
 // result does not depend on timing.
