@@ -15,7 +15,9 @@ Timing, per workload:
     the level sustained GEMM work settles at (timed at 10 launches after
     idle, 4096^3 ran 10-30 % slower than at steady state);
   * ``--warmup`` untimed launches, then exactly ``--steps`` launches between
-    two HIP events recorded on the launch stream (``value``, ``us``);
+    two HIP events recorded on the launch stream (``value``, ``us``); the GPU
+    is kept busy from the end of the ramp to the timed region (no
+    synchronisation or host-side metrics read with it idle in between);
   * ``--repeats`` further timings of ``--steps`` launches each, reported as
     min / median / max, so run-to-run noise is visible;
   * clocks: shader (per XCD) and memory clock sampled through amdsmi while
@@ -278,9 +280,11 @@ def _measure(torch, step, flops, nbytes, bound, args, stream, clocks):
     of the module docstring, for one launch function."""
 
     def timed(n):
+        # No synchronisation before the first event: the launches queued
+        # before it (warm-up, or the previous timing) keep the GPU busy up to
+        # the timed region, so its clock does not dip in an idle gap.
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         w0 = time.perf_counter()
         with torch.cuda.stream(stream):
             e0.record(stream)
@@ -290,19 +294,29 @@ def _measure(torch, step, flops, nbytes, bound, args, stream, clocks):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3, time.perf_counter() - w0  # us per launch
 
-    # clock ramp, then the warm-up launches
+    # clock ramp, then the warm-up launches.  The clock stamp (a read of the
+    # GPU metrics, ~ms on the host) is taken while queued launches run: taken
+    # with the GPU idle, the first timed launches ran ~2 % slower than the
+    # repeats after them.
     ramp_launches = 0
-    t_end = time.perf_counter() + args.ramp_s
+    t0 = time.perf_counter()
+    t_end = t0 + args.ramp_s
     with torch.cuda.stream(stream):
         while time.perf_counter() < t_end:
             for i in range(20):
                 step(ramp_launches + i)
             ramp_launches += 20
             torch.cuda.synchronize()
+        # a last batch of ramp launches, ~10 ms of GPU work, queued before the
+        # stamp so that the GPU is still busy while it is read
+        per_launch = (time.perf_counter() - t0) / max(ramp_launches, 1)
+        bridge = int(min(2000, max(20, 0.01 / max(per_launch, 1e-6))))
+        for i in range(bridge):
+            step(ramp_launches + i)
+        ramp_launches += bridge
+        t_begin = clocks.stamp() if clocks is not None else None
         for i in range(args.warmup):
             step(i)
-    torch.cuda.synchronize()
-    t_begin = clocks.stamp() if clocks is not None else None
     us, wall = timed(args.steps)
     reps = [timed(args.steps)[0] for _ in range(args.repeats)]
 
