@@ -215,6 +215,34 @@ def test_degenerate_shapes_on_the_host(lib):
     assert so.gemm_f16(0, 16, 8, None, 8, None, 8, fake, 16, None) == lib.GEMM_OK
 
 
+def test_config_name_storage_is_per_thread(lib):
+    """gemm_bf16_config_name returns per-thread static storage: threads
+    asking for different shapes at the same time each read their own name
+    (ctypes releases the GIL for the call, so the calls do overlap)."""
+    import threading
+
+    shapes = [(4096, 4096, 4096), (256, 8192, 28672), (1, 8192, 8192), (300, 520, 456),
+              (512, 512, 512), (64, 8192, 8192), (8192, 28672, 8192), (200, 8192, 8192)]
+    want = {sh: lib.config_name(*sh) for sh in shapes}
+    assert len(set(want.values())) > 4
+    errors = []
+
+    def worker(i):
+        for r in range(3000):
+            sh = shapes[(i + r) % len(shapes)]
+            got = lib.config_name(*sh)
+            if got != want[sh]:
+                errors.append((i, r, sh, got))
+                return
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(6)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+
+
 def test_product_path_never_imports_the_oracle():
     pkg = os.path.join(ROOT, "dense_gemm_bf16_amd")
     for dirpath, _, files in os.walk(pkg):
