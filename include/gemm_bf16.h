@@ -223,7 +223,10 @@ int gemm_bf16_reserve_workspace(size_t bytes, void* stream);
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* Free every workspace this library holds, on every device.  Synchronises
- * the streams they belong to first.  Returns a status code. */
+ * the streams they belong to first, so every stream that has made a split-K
+ * call (or reserved a workspace) must still exist when this is called:
+ * destroying a stream does not free its workspace, and a destroyed stream
+ * cannot be synchronised.  Returns a status code. */
 int gemm_bf16_release_workspace(void);
 
 #ifdef __cplusplus
