@@ -106,6 +106,29 @@ def test_argument_checks_need_no_device(lib):
                                    None) == lib.GEMM_OK
 
 
+def test_size_limits_are_refused_on_the_host(lib):
+    """Shapes and strides past the kernels' 32-bit limits come back as
+    GEMM_ERR_UNSUPPORTED before anything is enqueued: a 256-row tile's rows
+    of A or B spanning 2^31 - 4096 bytes or more, M, N or K of 2^31 or
+    more, or 2^31 or more workgroups."""
+    so = lib._lib
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call here is refused
+    big = b"t256x256x64_w2x2_s2_x3_p10_k1_g4"
+    ld = ((1 << 31) - 4096) // (256 * 2)  # 256 rows of ld elements: exactly the limit
+    assert ld % 8 == 0
+    unsupported = lib.GEMM_ERR_UNSUPPORTED
+    assert so.gemm_bf16_ex(big, 8, 8, 8, fake, ld, fake, 8, fake, 8, 0, None) == unsupported
+    assert so.gemm_bf16_ex(big, 8, 8, 8, fake, 8, fake, ld, fake, 8, 0, None) == unsupported
+    assert so.gemm_f16_ex(big, 8, 8, 8, fake, ld, fake, 8, fake, 8, 0, None) == unsupported
+    m31 = 1 << 31
+    assert so.gemm_bf16(m31, 8, 8, fake, 8, fake, 8, fake, 8, None) == unsupported
+    assert so.gemm_bf16(8, m31, 8, fake, 8, fake, 8, fake, m31, None) == unsupported
+    # 2^22 x 2^22 tiles of 256 x 256
+    n30 = 1 << 30
+    assert so.gemm_bf16_ex(big, n30, n30, 8, fake, 8, fake, 8, fake, n30, 0,
+                           None) == unsupported
+
+
 def test_noalloc_scratch_covers_every_automatic_plan(lib):
     """The automatic plans' split-K partials stay below the static scratch
     for every workload shape and a sweep of decode-like and ragged shapes,

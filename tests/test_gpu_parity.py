@@ -207,6 +207,54 @@ def test_no_writes_outside_c():
     assert np.array_equal(buf[1:-1, :N], ref16)
 
 
+BIG = "t256x256x64_w2x2_s2_x3_p10"
+# A 256-row tile's operand rows, plus the 4 KB a load's resource base may be
+# moved back by, must stay below 2^31 bytes (a 32-bit buffer offset with the
+# top bit marking an absent chunk): the largest row stride the 256-row tile
+# takes is the largest multiple of 8 elements below that.
+LD_MAX_256 = ((((1 << 31) - 4096) - 1) // (256 * 2)) // 8 * 8
+
+
+@pytest.mark.parametrize("plan", [BIG + "_k1_g4", BIG + "_k2_g4"])
+def test_largest_accepted_strides(plan):
+    """lda and ldb at the largest value the 256 x 256 tile accepts (2 GiB
+    per operand, NaN everywhere but the first K columns) and ldc = 2^23, so
+    C's byte offsets pass 2^32; the result is exact and nothing beyond the
+    first N columns of C changes.  One element more of lda or ldb is refused
+    before anything is enqueued."""
+    import torch
+
+    import dense_gemm_bf16_amd as g
+
+    M, N, K = 256, 256, 200
+    lda = ldb = LD_MAX_256
+    assert 256 * (lda + 8) * 2 >= (1 << 31) - 4096 > 256 * lda * 2
+    ldc = 1 << 23
+    A = int_bf16(M, K, seed=560)
+    B = int_bf16(N, K, seed=561)
+    ref16, _ = _oracle().gemm(A, B)
+    nan = np.array([0x7FC0], np.uint16).view(np.int16)[0]
+    dA = torch.full((M, lda), int(nan), dtype=torch.int16, device="cuda")
+    dB = torch.full((N, ldb), int(nan), dtype=torch.int16, device="cuda")
+    dA[:, :K].copy_(torch.from_numpy(A.view(np.int16)))
+    dB[:, :K].copy_(torch.from_numpy(B.view(np.int16)))
+    canary = 0x5A5A
+    dC = torch.full((M, ldc), canary, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    print(plan, "lda", lda, "ldc", ldc, flush=True)
+    g.gemm_bf16_ex(plan, M, N, K, dA, lda, dB, ldb, dC, ldc)
+    torch.cuda.synchronize()
+    got = dC[:, :N].cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref16), int(np.count_nonzero(got != ref16))
+    assert np.all(dC[:, N:N + 512].cpu().numpy() == canary)
+    assert np.all(dC[:, ldc - 64:].cpu().numpy() == canary)
+    for la, lb in [(lda + 8, ldb), (lda, ldb + 8)]:
+        rc = g.gemm_bf16_status(M, N, K, dA, la, dB, lb, dC, ldc, config=plan)
+        assert rc == g.GEMM_ERR_UNSUPPORTED, (la, lb, rc)
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+
+
 def test_k_zero_gives_zeros():
     import torch
 
