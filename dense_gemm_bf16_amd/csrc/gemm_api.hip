@@ -83,6 +83,8 @@ int64_t partial_ld(int64_t N) { return (N + 7) / 8 * 8; }
 
 
 size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
+  if (p.split_n > 0)  // hybrid: only the columns past split_n are split
+    return (size_t)p.tail_splits * (size_t)M * (size_t)partial_ld(N - p.split_n) * 4;
   if (p.splits <= 1) return 0;
   return (size_t)p.splits * (size_t)M * (size_t)partial_ld(N) * 4;
 }
@@ -117,6 +119,16 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 //    stores weigh more than the smaller tile costs (512 x 4096 x 4096: 128 x
 //    128 split 2, 26.5 vs 28.6 us).  Then direct-to-LDS 128 x 128 tiles with
 //    a four-slot ring, split to about 256 workgroups.
+//  * and where the tiles chosen above (unsplit) fill their last pass over
+//    the CUs only in part, a hybrid plan ("_h<S>"): the whole passes, taken
+//    as whole tile columns, run unsplit, and the tile columns left over run
+//    as a second call with K split S ways, when those tiles times S fit in
+//    one pass.  The left-over pass then takes 1/S of a tile's time plus the
+//    split's partial round trip.  Measured (as the two calls, against the
+//    plain plan): 2048 x 10240 x 8192 329.5 -> 272.1 us, 1024 x 10240 x 8192
+//    195.3 -> 156.6, 512 x 10240 x 8192 111.7 -> 91.0, 1024 / 2048 / 4096 x
+//    5376 x 5376 -11 to -12 %, 4096 x 10240 x 8192 -2.3 %, 2048 x 28672 x
+//    8192 -3.2 %.
 // All three direct-to-LDS tiles run with 16 x 16 x 32 MFMAs: at the same
 // cycles per FLOP the chip holds a higher clock under its power limit with
 // them, and measured against the 32 x 32 x 16 form of the same tiles they
@@ -176,13 +188,35 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
     const int64_t per = (k_tiles + p->splits - 1) / p->splits;
     p->splits = (int)((k_tiles + per - 1) / per);
   }
+  // Hybrid: the first whole passes over the CUs, as whole tile columns, run
+  // unsplit; the columns after them form a second call with K split.  Only
+  // where both parts are non-empty and the tail still splits after the
+  // same clamping as above; otherwise the plain plan.
+  p->split_n = 0;
+  if (p->tail_splits > 1 && p->splits == 1 && p->persist == 0) {
+    const int64_t tiles_m = (M + p->tile->bm - 1) / p->tile->bm;
+    const int64_t tiles_n = (N + p->tile->bn - 1) / p->tile->bn;
+    const int64_t head_cols = tiles_m > 0 ? (tiles_m * tiles_n / kCUs) * kCUs / tiles_m : 0;
+    int64_t s = p->tail_splits < k_tiles ? p->tail_splits : k_tiles;
+    if (s > 1) {
+      const int64_t per = (k_tiles + s - 1) / s;
+      s = (k_tiles + per - 1) / per;
+    }
+    if (head_cols > 0 && head_cols < tiles_n && s > 1) {
+      p->tail_splits = (int)s;
+      p->split_n = head_cols * p->tile->bn;
+    }
+  }
+  if (p->split_n == 0) p->tail_splits = 0;
   int n = snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
   if (p->k_rot > 0 && n > 0 && n < (int)sizeof p->name)
     n += snprintf(p->name + n, sizeof p->name - n, "_r%d", p->k_rot);
   if (p->persist > 0 && n > 0 && n < (int)sizeof p->name)
     n += snprintf(p->name + n, sizeof p->name - n, "_P%d", p->persist);
   if (p->stream_b > 0 && n > 0 && n < (int)sizeof p->name)
-    snprintf(p->name + n, sizeof p->name - n, "_n1");
+    n += snprintf(p->name + n, sizeof p->name - n, "_n1");
+  if (p->split_n > 0 && n > 0 && n < (int)sizeof p->name)
+    snprintf(p->name + n, sizeof p->name - n, "_h%d", p->tail_splits);
 }
 
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out);
@@ -236,19 +270,33 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
       p.k_rot = 0;
     }
   }
+  if (M > 64 && p.splits == 1) {
+    // A last pass over the CUs that the tiles fill only in part: run the
+    // whole passes (as whole tile columns) unsplit and the columns left
+    // over with K split, when that fits the left-over tiles into one pass.
+    const int64_t tiles_m = (M + p.tile->bm - 1) / p.tile->bm;
+    const int64_t tiles = tiles_of(p.tile, M, N);
+    const int64_t head_tiles = tiles_m > 0 ? (tiles / kCUs) * kCUs / tiles_m * tiles_m : 0;
+    const int64_t tail_tiles = tiles - head_tiles;
+    if (head_tiles > 0 && tail_tiles > 0) {
+      const int s = choose_splits(tail_tiles, (K + p.tile->bk - 1) / p.tile->bk);
+      if (s > 1 && tail_tiles * s <= kCUs) p.tail_splits = s;
+    }
+  }
   finish_plan(&p, M, N, K);
   return p;
 }
 
-// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>][_n<0|1>]" where
-// tile is a table name (_P: a persistent grid of that many workgroups
+// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>][_n<0|1>][_h<splits>]"
+// where tile is a table name (_P: a persistent grid of that many workgroups
 // walking the tiles; only for tiles built with it, bf16 operands, and never
-// split.  _n1: non-temporal B loads, only for tiles built with them).
+// split.  _n1: non-temporal B loads, only for tiles built with them.  _h:
+// the hybrid of finish_plan, only with _k1 and no _P).
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out) {
   char buf[64];
   if (strlen(name) >= sizeof buf) return false;
   strcpy(buf, name);
-  int splits = 1, group = 4, rot = 0, persist = 0, stream = 0;
+  int splits = 1, group = 4, rot = 0, persist = 0, stream = 0, tail = 0;
   for (;;) {
     char* u = strrchr(buf, '_');
     if (!u) break;
@@ -268,6 +316,9 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
     } else if (u[1] == 'n' && sscanf(u + 2, "%d", &v) == 1 && (v == 0 || v == 1)) {
       stream = v;
       *u = 0;
+    } else if (u[1] == 'h' && sscanf(u + 2, "%d", &v) == 1 && v >= 0) {
+      tail = v;
+      *u = 0;
     } else {
       break;
     }
@@ -276,12 +327,14 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
   if (!t) return false;
   if (persist > 0 && (!t->persist || splits > 1)) return false;
   if (stream && !t->stream) return false;
+  if (tail > 1 && (splits > 1 || persist > 0)) return false;
   out->tile = t;
   out->splits = splits;
   out->group_m = group;
   out->k_rot = rot;
   out->persist = persist;
   out->stream_b = stream;
+  out->tail_splits = tail;
   finish_plan(out, M, N, K);
   return true;
 }
@@ -300,12 +353,13 @@ int check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   return GEMM_OK;
 }
 
-// `fixed_ws`: the device address of a caller-side partial buffer of
-// `fixed_bytes` bytes to use instead of the per-stream workspace (the
-// no-allocation entry point), or NULL.
-int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-        const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
-        hipStream_t stream, void* fixed_ws = nullptr, size_t fixed_bytes = 0) {
+// One launch plan (not hybrid) on the whole of C.  `fixed_ws`: the device
+// address of a caller-side partial buffer of `fixed_bytes` bytes to use
+// instead of the per-stream workspace (the no-allocation entry point), or
+// NULL.
+int run_one(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+            const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
+            hipStream_t stream, void* fixed_ws, size_t fixed_bytes) {
   const TileConfig& t = *p.tile;
   if (half && !t.f16) return GEMM_ERR_UNSUPPORTED;
   if (p.persist > 0 && (half || !t.persist || p.splits > 1)) return GEMM_ERR_UNSUPPORTED;
@@ -378,6 +432,33 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
     if (e != hipSuccess) return hip_fail(e);
   }
   return GEMM_OK;
+}
+
+// A plan on C: a hybrid plan as two calls on column ranges, each a plain
+// plan of the same tile -- columns [split_n, N) with K split tail_splits
+// ways first (it is the part that may need a workspace, so an error there
+// leaves nothing enqueued), then columns [0, split_n) unsplit.  The two
+// ranges share no element of C, so each element's sum is that of the plan
+// that covers it.
+int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+        const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
+        hipStream_t stream, void* fixed_ws = nullptr, size_t fixed_bytes = 0) {
+  if (p.split_n <= 0 || p.split_n >= N)
+    return run_one(p, M, N, K, A, lda, B, ldb, C, ldc, out_f32, half, stream, fixed_ws,
+                   fixed_bytes);
+  const int64_t n1 = p.split_n;
+  Plan part = p;
+  part.split_n = 0;
+  part.tail_splits = 0;
+  part.splits = p.tail_splits;
+  const uint16_t* B1 = (const uint16_t*)B + n1 * ldb;
+  uint8_t* C1 = (uint8_t*)C + n1 * (out_f32 ? 4 : 2);
+  int rc = run_one(part, M, N - n1, K, A, lda, B1, ldb, C1, ldc, out_f32, half, stream,
+                   fixed_ws, fixed_bytes);
+  if (rc != GEMM_OK) return rc;
+  part.splits = 1;
+  return run_one(part, M, n1, K, A, lda, B, ldb, C, ldc, out_f32, half, stream, fixed_ws,
+                 fixed_bytes);
 }
 
 // The plan of a call: the named configuration, or the automatic choice.

@@ -38,6 +38,11 @@ struct Plan {
   int k_rot;    // K-step rotation stride per tile, 0 = none
   int persist;  // persistent grid of this many workgroups (a multiple of 8), 0 = none
   int stream_b; // 1: B loads non-temporal (where the tile is built with it)
+  // Hybrid: the tile columns that fill whole passes over the CUs run
+  // unsplit, the columns from split_n on run as a second call with K split
+  // tail_splits ways (0 / 0: not hybrid).
+  int tail_splits;
+  int64_t split_n;
   char name[64];
 };
 

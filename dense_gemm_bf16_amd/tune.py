@@ -4,14 +4,16 @@ the library's plan choice consults first (``csrc/gemm_tuned.inc``).
 
 A plan is a configuration name of the library (``gemm_bf16_config_at``)
 plus the K split count, raster grouping and K-step rotation
-(``<tile>_k<S>_g<G>[_r<R>]``), exactly the names ``gemm_bf16_ex`` accepts.
+(``<tile>_k<S>_g<G>[_r<R>][_n1][_h<S>]``), exactly the names ``gemm_bf16_ex``
+accepts.
 For each shape the sweep
 
 1. enumerates candidates (every tile built for the operand type, except
    the LDS-layout ablation tiles; split counts that keep at least four
    K-steps per slice and at most ~4 workgroups per CU; GROUP_M 4 and 8;
    rotation off and on; with one row of tiles, non-temporal B loads off and
-   on where the tile is built with them),
+   on where the tile is built with them; with more than one pass of tiles
+   over the CUs and the last one partial, the hybrid plans "_h2" .. "_h4"),
 2. times every candidate briefly (HIP events on one stream, after a warm-up
    long enough for the clock to settle; memory-bound shapes cycle through
    copies of B larger than the 256 MB Infinity Cache, as ``bench.py`` does),
@@ -74,12 +76,18 @@ def candidates(M: int, N: int, K: int, tiles: list[str], cus: int = 256,
             # GROUP_M orders tile rows; with one row of tiles every value
             # gives the same launch, so time only one
             one_row = -(-M // bm) == 1
+            # more than one pass of tiles, the last one partial: also the
+            # hybrid plans (whole passes unsplit, the columns left over with
+            # K split h ways)
+            hybrid = s == 1 and n_tiles > cus and n_tiles % cus != 0
             for g in ((4, 8) if not one_row else (4,)):
                 for r in (0, 1):
                     name = f"{tile}_k{s}_g{g}" + (f"_r{r}" if r else "")
                     out.append(name)
                     if one_row and tile in stream_tiles:
                         out.append(name + "_n1")
+                    if hybrid:
+                        out += [f"{name}_h{h}" for h in (2, 3, 4) if k_tiles // h >= 4]
     return out
 
 

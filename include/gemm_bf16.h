@@ -37,7 +37,9 @@
  * Ownership.  The caller owns A, B and C; the library neither frees nor
  * retains them.  C must not overlap A or B.  When a shape's configuration
  * splits K, the fp32 partial sums of the S slices (S * M * roundup8(N) * 4
- * bytes) go to a workspace the library owns per (device, stream): allocated
+ * bytes, or S * M * roundup8(N - N1) * 4 for a hybrid plan that splits only
+ * the columns from N1 on; see gemm_bf16_config_name) go to a workspace the
+ * library owns per (device, stream): allocated
  * on first need and grown when a larger one is needed.  Growth allocates a
  * new buffer and keeps the old one alive (work already queued, or a graph
  * captured earlier, may still use it); all of them are freed by
@@ -115,8 +117,21 @@ int gemm_bf16_ex(const char* config,
  * same for both operand types) would choose for this shape, e.g.
  * "t256x256x64_w2x2_s2_x3_p10_k1_g4": tile BM x BN x BK, waves, ring stages,
  * LDS swizzle, load schedule, then K splits and GROUP_M (and "_r<n>", the
- * K-step rotation, when on, and "_n1" when B is loaded non-temporally).
+ * K-step rotation, when on, "_n1" when B is loaded non-temporally, and
+ * "_h<S>" for a hybrid plan).
  * Per-thread static storage, valid until the thread's next call; never NULL.
+ *
+ * "_h<S>" (a hybrid plan; with "_k1" only, and not with "_P"): where the
+ * tiles fill their last pass over the GPU's 256 compute units only in part,
+ * the tile columns that make up the whole passes (N1 = the largest number
+ * of whole tile columns within them, times the tile width) are computed
+ * unsplit, and columns N1 .. N-1 as a second launch with K split S ways and
+ * the fixed-order reduction.  Each element's sum is that of the part that
+ * covers it, so results are reproducible run to run; the columns from N1 on
+ * may differ from the unsplit plan's in the last bits, as any split does.
+ * The automatic choice uses it when the left-over tiles times S fit in one
+ * pass.  Named on a shape where it does not apply (whole passes, one pass or
+ * less, or too few K-steps to split), it is dropped and the plain plan runs.
  *
  * "_n1" (accepted by gemm_bf16_ex / gemm_f16_ex on the tiles built for it:
  * the 256 x 128 direct-to-LDS tile and the M <= 64 tiles) marks B's loads

@@ -139,8 +139,54 @@ def test_noalloc_scratch_covers_every_automatic_plan(lib):
     for M in (1, 17, 64, 65, 128, 129, 200, 256, 300, 512, 1024):
         for N in (128, 1000, 4096, 8192, 10240, 19200, 28672):
             shapes.append((M, N, 8192))
+    # hybrid plans (a split tail after whole passes of tiles)
+    for M in (2048, 3000, 4096, 10240, 16384):
+        for N in (2048, 5376, 8192, 10240, 28672):
+            for K in (5376, 8192):
+                shapes.append((M, N, K))
     for M, N, K in shapes:
         assert lib.workspace_size(M, N, K) <= lib.GEMM_NOALLOC_SCRATCH_BYTES, (M, N, K)
+
+
+def test_hybrid_plan_names_on_the_host(lib):
+    """Hybrid plans (_h<S>): the automatic choice where the tiles fill their
+    last pass over the 256 CUs only in part and the left-over columns' tiles
+    times S fit in one pass; never where the passes are whole.  Named, they
+    are accepted with _k1 (M = 0, so nothing is launched) and refused with a
+    split or a persistent grid."""
+    so = lib._lib
+    fake = ctypes.c_void_p(0x10000)
+    big = "t256x256x64_w2x2_s2_x3_p10"
+    assert lib.config_name(2048, 10240, 8192) == big + "_k1_g4_h4"
+    assert lib.config_name(4096, 10240, 8192) == big + "_k1_g4_h2"
+    assert lib.workspace_size(2048, 10240, 8192) == 4 * 2048 * (10240 - 8192) * 4
+    for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 28672, 8192),
+                    (1024, 28672, 8192), (256, 8192, 8192), (300, 520, 456)]:
+        assert "_h" not in lib.config_name(M, N, K), (M, N, K)
+    pat = re.compile(r"^t(\d+)x(\d+)x\d+_.*_k1_g\d+(_r\d+)?_h(\d+)$")
+    seen = 0
+    for M in (512, 1024, 2048, 3000, 4096, 10240):
+        for N in (2048, 5376, 8192, 10240, 28672):
+            for K in (5376, 8192):
+                m = pat.match(lib.config_name(M, N, K))
+                if not m:
+                    continue
+                seen += 1
+                bm, bn, S = int(m.group(1)), int(m.group(2)), int(m.group(4))
+                tiles_m, tiles_n = -(-M // bm), -(-N // bn)
+                head_cols = (tiles_m * tiles_n // 256) * 256 // tiles_m
+                assert 0 < head_cols < tiles_n
+                assert (tiles_n - head_cols) * tiles_m * S <= 256, (M, N, K)
+                assert lib.workspace_size(M, N, K) == S * M * (N - head_cols * bn) * 4
+    assert seen >= 10
+
+    def rc(name):
+        return so.gemm_bf16_ex(name.encode(), 0, 8, 8, None, 8, None, 8, fake, 8, 0, None)
+
+    assert rc(big + "_k1_g4_h3") == lib.GEMM_OK
+    assert rc(big + "_k1_g4_h0") == lib.GEMM_OK
+    assert rc(big + "_k2_g4_h3") == lib.GEMM_ERR_UNSUPPORTED
+    assert rc(big + "_k1_g4_P256_h2") == lib.GEMM_ERR_UNSUPPORTED
 
 
 def test_persistent_plan_names_on_the_host(lib):
@@ -199,7 +245,7 @@ def test_config_names(lib):
 
     for w in WORKLOADS.values():
         chosen = lib.config_name(w.M, w.N, w.K)
-        m = re.match(r"^(.*)_k(\d+)_g(\d+)(_r\d+)?(_n1)?$", chosen)
+        m = re.match(r"^(.*)_k(\d+)_g(\d+)(_r\d+)?(_n1)?(_h\d+)?$", chosen)
         assert m and m.group(1) in names, chosen
         S = int(m.group(2))
         ws = lib.workspace_size(w.M, w.N, w.K)
@@ -219,7 +265,7 @@ def test_f16_configs(lib):
     shapes = [(w.M, w.N, w.K) for w in WORKLOADS.values()]
     shapes += [(1, 16, 8), (64, 64, 64), (65, 4096, 4096), (224, 8192, 1024), (8192, 256, 64)]
     for M, N, K in shapes:
-        tile = re.match(r"^(.*)_k\d+_g\d+(_r\d+)?(_n1)?$", lib.config_name(M, N, K)).group(1)
+        tile = re.match(r"^(.*)_k\d+_g\d+(_r\d+)?(_n1)?(_h\d+)?$", lib.config_name(M, N, K)).group(1)
         assert tile in f16, (M, N, K, tile)
     assert lib.f16_config_at(len(f16)) is None and lib.f16_config_at(-1) is None
 

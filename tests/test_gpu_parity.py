@@ -491,3 +491,113 @@ def test_stream_b_with_several_tile_rows_is_still_exact():
     ref16, _ = _oracle().gemm(A, B)
     got = run_gemm(A, B, config="t256x128x64_w2x2_s3_x3_p10_k2_g4_n1")
     assert check_bf16(got, ref16, None, K, exact=True)["ok"]
+
+
+# ------------------------------------------------------------ hybrid plans
+# "_h<S>": the tile columns that fill whole passes over the 256 CUs run
+# unsplit, the columns after them as a second call with K split S ways.
+# Each shape below has a little more than one pass of tiles of its
+# configuration (3 rows of tiles x 90 columns, the last column ragged), so
+# the hybrid splits at column 85 of 90.
+HYBRID_CASES = [  # (tile, M, N)
+    ("t256x256x64_w2x2_s2_x3_p10", 520, 22920),
+    ("t256x128x64_w2x2_s3_x3_p10", 520, 11460),
+    ("t128x128x64_w2x2_s4_x3_p10", 300, 11460),
+]
+
+
+@pytest.mark.parametrize("tile,M,N", HYBRID_CASES)
+def test_hybrid_plans_bit_exact(tile, M, N):
+    """Integer inputs with K = 456 (a partial last K-step): the hybrid plan
+    with the tail split 2 and 3 ways is bit-exact in bf16 and fp32 output,
+    and so is the no-allocation entry point with it."""
+    import torch
+
+    import dense_gemm_bf16_amd as g
+
+    K = 456
+    A = int_bf16(M, K, seed=1500 + M)
+    B = int_bf16(N, K, seed=1501 + N)
+    ref16, ref64 = _oracle().gemm(A, B)
+    for plan in (tile + "_k1_g4_h2", tile + "_k1_g4_h3"):
+        got = run_gemm(A, B, config=plan)
+        rep = check_bf16(got, ref16, None, K, exact=True)
+        print(plan, M, N, rep, flush=True)
+        assert rep["ok"], (plan, rep)
+        got32 = run_gemm(A, B, config=plan, out_f32=True)
+        assert check_f32(got32, ref64, K, exact=True)["ok"], plan
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    ldc = (N + 7) // 8 * 8
+    dC = torch.zeros((M, ldc), dtype=torch.int16, device="cuda")
+    g.gemm_bf16_ex_noalloc(tile + "_k1_g4_h3", M, N, K, dA, K, dB, K, dC, ldc)
+    torch.cuda.synchronize()
+    assert np.array_equal(dC[:, :N].cpu().numpy().view(np.uint16), ref16)
+
+
+@pytest.mark.parametrize("tile,M,N", HYBRID_CASES[:1])
+def test_hybrid_head_matches_plain_plan_on_normal_inputs(tile, M, N):
+    """N(0,1) inputs: the unsplit head columns are the plain plan's bits (same
+    tiles, same summation order), and the whole result meets the ulp
+    criterion against the oracle."""
+    K = 1000
+    A = normal_bf16(M, K, seed=1510)
+    B = normal_bf16(N, K, seed=1511)
+    hyb = run_gemm(A, B, config=tile + "_k1_g4_h3")
+    plain = run_gemm(A, B, config=tile + "_k1_g4")
+    hyb32 = run_gemm(A, B, config=tile + "_k1_g4_h3", out_f32=True)
+    plain32 = run_gemm(A, B, config=tile + "_k1_g4", out_f32=True)
+    bm, bn = int(tile[1:].split("x")[0]), int(tile.split("x")[1])
+    tiles_m, tiles_n = -(-M // bm), -(-N // bn)
+    n1 = (tiles_m * tiles_n // 256) * 256 // tiles_m * bn
+    assert 0 < n1 < N
+    assert np.array_equal(hyb[:, :n1], plain[:, :n1])
+    assert np.array_equal(hyb32[:, :n1], plain32[:, :n1])
+    # the tail's sums run in another order (split K)
+    assert np.count_nonzero(hyb32[:, n1:] != plain32[:, n1:]) > 0
+    ref16, ref64 = _oracle().gemm(A, B)
+    rep = check_bf16(hyb, ref16, ref64, K)
+    print(tile, "hybrid", rep, flush=True)
+    assert rep["ok"], rep
+    assert check_f32(hyb32, ref64, K)["ok"]
+
+
+def test_hybrid_f16_bit_exact():
+    """The hybrid plan over fp16 operands (integers in [-16, 16], so fp16
+    rounding of sums above 2048 happens in both parts' epilogues)."""
+    tile, M, N = HYBRID_CASES[2]
+    K = 456
+    A = int_bf16(M, K, seed=1520, lo=-16, hi=16, fmt="f16")
+    B = int_bf16(N, K, seed=1521, lo=-16, hi=16, fmt="f16")
+    ref16, ref64 = _oracle().gemm(A, B, fmt="f16")
+    got = run_gemm(A, B, config=tile + "_k1_g4_h3", fmt="f16")
+    rep = check_bf16(got, ref16, None, K, exact=True, fmt="f16")
+    print("f16 hybrid", rep, flush=True)
+    assert rep["ok"], rep
+
+
+def test_automatic_hybrid_plan_on_a_qkv_shape():
+    """2048 x 10240 x 8192 (a 70B-class fused QKV projection at 2048 tokens):
+    320 tiles of 256 x 256, so the automatic plan is hybrid; full rows and
+    columns on both sides of the split column are checked against the
+    oracle."""
+    import dense_gemm_bf16_amd as g
+
+    M, N, K = 2048, 10240, 8192
+    plan = g.config_name(M, N, K)
+    print("plan", plan, flush=True)
+    assert plan.endswith("_h4"), plan
+    A = normal_bf16(M, K, seed=1530)
+    B = normal_bf16(N, K, seed=1531, std=K ** -0.5)
+    got = run_gemm(A, B)
+    o = _oracle()
+    rows = np.array([0, 1, 255, 256, 1000, 2047])
+    cols = np.array([0, 8191, 8192, 8193, 9000, 10239])
+    r16, r64 = o.gemm(np.ascontiguousarray(A[rows]), B)
+    rep = check_bf16(got[rows], r16, r64, K, 1.0, K ** -0.5)
+    print("rows", rep, flush=True)
+    assert rep["ok"], rep
+    c16, c64 = o.gemm(A, np.ascontiguousarray(B[cols]))
+    rep = check_bf16(got[:, cols], c16, c64, K, 1.0, K ** -0.5)
+    print("cols", rep, flush=True)
+    assert rep["ok"], rep

@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TABLE = os.path.join(ROOT, "dense_gemm_bf16_amd", "csrc", "gemm_tuned.inc")
-PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d+)_k(\d+)_g(\d+)(_r\d+)?(_n1)?$")
+PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d+)_k(\d+)_g(\d+)(_r\d+)?(_n1)?(_h\d+)?$")
 ROW = re.compile(r'^\{(\d+), (\d+), (\d+), "([^"]+)"\},$')
 
 
@@ -63,6 +63,33 @@ def test_stream_candidates_only_for_one_row_of_tiles(lib):
                 assert tile in st and -(-M // parse_tile(tile)[0]) == 1, p
     assert any(p.endswith("_n1") for p in candidates(256, 8192, 8192, tiles, stream_tiles=st))
     assert not any(p.endswith("_n1") for p in candidates(4096, 4096, 4096, tiles, stream_tiles=st))
+
+
+def test_hybrid_candidates_only_past_one_partial_pass(lib):
+    """_h candidates exist exactly for unsplit plans whose tiles make more
+    than one pass over the 256 CUs with the last pass partial, and every one
+    is a name the library accepts (M = 0, so nothing is launched)."""
+    import ctypes
+
+    from dense_gemm_bf16_amd.tune import candidates, parse_tile
+
+    tiles = lib.config_names()
+    fake = ctypes.c_void_p(0x10000)
+    for M, N, K in [(2048, 10240, 8192), (4096, 4096, 4096), (256, 8192, 8192),
+                    (1024, 5376, 5376)]:
+        for p in candidates(M, N, K, tiles):
+            if "_h" not in p:
+                continue
+            m = PLAN.match(p)
+            assert m and m.group(2) == "1", p
+            bm, bn, _ = parse_tile(m.group(1))
+            n_tiles = -(-M // bm) * -(-N // bn)
+            assert n_tiles > 256 and n_tiles % 256, p
+            rc = lib._lib.gemm_bf16_ex(p.encode(), 0, 64, 64, fake, 64, fake, 64, fake, 64, 0,
+                                       None)
+            assert rc == lib.GEMM_OK, p
+    assert any("_h" in p for p in candidates(2048, 10240, 8192, tiles))
+    assert not any("_h" in p for p in candidates(4096, 4096, 4096, tiles))
 
 
 def test_written_table_format(tmp_path):
