@@ -90,8 +90,12 @@ size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 }
 
 // ------------------------------------------------------------ config choice
-// Static shape -> configuration rules, from sweeps on MI355X (HIP events,
-// cold B for the memory-bound shapes):
+// Shape -> configuration, from sweeps on MI355X (HIP events, cold B for the
+// memory-bound shapes).  The tuned table first (exact shapes); for M > 256
+// the cost model below (model_plan), which picks among the direct-to-LDS
+// tiles, split counts and hybrids; otherwise these rules (for M > 256 they
+// were the choice before the model, which keeps their plans for 4096^3 and
+// the M = 8192 prefill shapes):
 //  * M <= 64 (small decode batches): the small-M kernel, one workgroup per
 //    BM x 32 block over all of K (BM = 32 up to M = 32, else 64), so
 //    N = 8192 gives 256 workgroups with no split-K pass; K-step rotation on
@@ -221,6 +225,103 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
 
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out);
 
+// ------------------------------------------------------- plan cost model
+// For M > 256 the plan is the cheapest under a model of a launch's time on
+// MI355X, fitted (least squares on log time) to 1,000 timings of 77 shapes:
+// M from 320 to 6144, N x K among 4096 x 4096, 14336 x 4096, 4096 x 14336,
+// 8192 x 8192, 10240 x 8192, 5376 x 5376 and 28672 x 8192, each direct-to-LDS
+// tile unsplit, split 2-8 and hybrid.  RMS error 4.5 %; on 42 other shapes
+// (M 288-5120, N x K with N or K of 3072-16384) its choice ran within 0.1 %
+// of the fastest plan timed (geometric mean; 3.5 % at worst), against 7.2 %
+// (and up to 50 %) for the earlier rules.
+//
+// A launch of `tiles` tiles split S ways runs units = tiles * S workgroups,
+// one per CU at a time: each pass over the 256 CUs costs a unit's time,
+// steps * step_us + tile_us (steps: K-steps per slice; tile_us: first loads
+// and epilogue), and a last pass with a fraction f of the CUs busy costs
+// kPartialPass + (1 - kPartialPass) * f of a full one (fewer workgroups
+// share L2, HBM and the power budget).  A split adds the partial slices'
+// round trip (written by the GEMM, read by the reduction) and the
+// reduction's launch.
+struct TileCost {
+  const char* name;
+  double step_us, tile_us;
+};
+constexpr TileCost kTileCosts[] = {
+    {kBig, 1.4295, 2.6456}, {kMid, 0.8187, 1.9745}, {kMid128, 0.4817, 1.8138}};
+constexpr double kPartialPass = 0.6767;
+constexpr double kLaunchUs = 1.1184;
+constexpr double kSplitUs = 1.4115;
+constexpr double kSplitUsPerMB = 0.3239;  // per MB of partial slices
+constexpr int64_t kModelMinM = 257;
+
+// K splits as finish_plan equalises them: ceil(k_tiles / S) steps a slice.
+int64_t even_splits(int64_t S, int64_t k_tiles) {
+  if (S > k_tiles) S = k_tiles;
+  if (S <= 1) return 1;
+  const int64_t per = (k_tiles + S - 1) / S;
+  return (k_tiles + per - 1) / per;
+}
+
+double launch_cost(const TileCost& c, int64_t tiles, int64_t S, int64_t k_tiles, int64_t M,
+                   int64_t N) {
+  const int64_t units = tiles * S;
+  const int64_t steps = (k_tiles + S - 1) / S;
+  double passes = (double)(units / kCUs);
+  if (units % kCUs) passes += kPartialPass + (1 - kPartialPass) * (double)(units % kCUs) / kCUs;
+  double t = (steps * c.step_us + c.tile_us) * passes + kLaunchUs;
+  if (S > 1) t += kSplitUs + kSplitUsPerMB * (double)(S * M * partial_ld(N) * 4) * 1e-6;
+  return t;
+}
+
+// The cheapest plan under the model: each direct-to-LDS tile unsplit, with
+// K split 2, 3, 4, 6 or 8 ways (at least 8 K-steps a slice, at most 4
+// workgroups per CU, partials within the no-allocation scratch), and the
+// hybrids of an unsplit plan whose last pass is partial, its left-over
+// columns split 2, 3, 4, 6 or 8 ways.
+Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
+  Plan best{};
+  double best_t = 0;
+  auto consider = [&](const TileConfig* t, int64_t S, int64_t h, double cost) {
+    if (best.tile && cost >= best_t) return;
+    best = Plan{};
+    best.tile = t;
+    best.splits = (int)S;
+    best.tail_splits = (int)h;
+    best.group_m = 4;
+    best_t = cost;
+  };
+  for (const TileCost& c : kTileCosts) {
+    const TileConfig* t = find_tile_config(c.name);
+    if (!t || (half && !t->f16)) continue;
+    const int64_t kt = (K + t->bk - 1) / t->bk;
+    const int64_t tm = (M + t->bm - 1) / t->bm, tn = (N + t->bn - 1) / t->bn;
+    const int64_t tiles = tm * tn;
+    for (int64_t S : {1, 2, 3, 4, 6, 8}) {
+      if (S > 1 && (kt / S < 8 || tiles * S > 4 * kCUs)) continue;
+      const int64_t s = even_splits(S, kt);
+      if (S > 1 && s <= 1) continue;
+      if (s > 1 && (size_t)(s * M * partial_ld(N) * 4) > GEMM_NOALLOC_SCRATCH_BYTES) continue;
+      consider(t, s, 0, launch_cost(c, tiles, s, kt, M, N));
+    }
+    if (tiles > kCUs && tiles % kCUs) {
+      const int64_t head_cols = (tiles / kCUs) * kCUs / tm;
+      if (head_cols <= 0 || head_cols >= tn) continue;
+      const int64_t n1 = head_cols * t->bn;
+      for (int64_t h : {2, 3, 4, 6, 8}) {
+        const int64_t hs = even_splits(h, kt);
+        if (hs <= 1) continue;
+        if ((size_t)(hs * M * partial_ld(N - n1) * 4) > GEMM_NOALLOC_SCRATCH_BYTES) continue;
+        consider(t, 1, hs,
+                 launch_cost(c, tm * head_cols, 1, kt, M, n1) +
+                     launch_cost(c, tm * (tn - head_cols), hs, kt, M, N - n1));
+      }
+    }
+  }
+  return best;
+}
+
+
 // The plan for a shape: the tuned table's entry if there is one (and its
 // tile is built for the operand type), else the rules.
 Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
@@ -234,6 +335,13 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
   p.group_m = 4;
   const TileConfig* big = find_tile_config(kBig);
   const int64_t big_tiles = tiles_of(big, M, N);
+  if (M >= kModelMinM) {
+    Plan m = model_plan(M, N, K, half);
+    if (m.tile) {
+      finish_plan(&m, M, N, K);
+      return m;
+    }
+  }
   if (M <= 64) {
     // One BM x 32 strip per workgroup while the strips fit in one pass over
     // the CUs (and BM x 32 strips re-read little A: M <= 48); otherwise

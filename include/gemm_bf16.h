@@ -129,8 +129,9 @@ int gemm_bf16_ex(const char* config,
  * the fixed-order reduction.  Each element's sum is that of the part that
  * covers it, so results are reproducible run to run; the columns from N1 on
  * may differ from the unsplit plan's in the last bits, as any split does.
- * The automatic choice uses it when the left-over tiles times S fit in one
- * pass.  Named on a shape where it does not apply (whole passes, one pass or
+ * The automatic choice weighs it against the plain plans: for M > 256 with
+ * a model of launch time fitted on MI355X, for smaller M when the left-over
+ * tiles times S fit in one pass.  Named on a shape where it does not apply (whole passes, one pass or
  * less, or too few K-steps to split), it is dropped and the plain plan runs.
  *
  * "_n1" (accepted by gemm_bf16_ex / gemm_f16_ex on the tiles built for it:

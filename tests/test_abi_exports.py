@@ -149,17 +149,16 @@ def test_noalloc_scratch_covers_every_automatic_plan(lib):
 
 
 def test_hybrid_plan_names_on_the_host(lib):
-    """Hybrid plans (_h<S>): the automatic choice where the tiles fill their
-    last pass over the 256 CUs only in part and the left-over columns' tiles
-    times S fit in one pass; never where the passes are whole.  Named, they
-    are accepted with _k1 (M = 0, so nothing is launched) and refused with a
-    split or a persistent grid."""
+    """Hybrid plans (_h<S>): chosen automatically on shapes whose unsplit
+    tiles make more than one pass over the 256 CUs with the last one
+    partial, never where the passes are whole; their split column lies
+    strictly inside N and their partials fit the no-allocation scratch.
+    Named, they are accepted with _k1 (M = 0, so nothing is launched) and
+    refused with a split or a persistent grid."""
     so = lib._lib
     fake = ctypes.c_void_p(0x10000)
     big = "t256x256x64_w2x2_s2_x3_p10"
-    assert lib.config_name(2048, 10240, 8192) == big + "_k1_g4_h4"
-    assert lib.config_name(4096, 10240, 8192) == big + "_k1_g4_h2"
-    assert lib.workspace_size(2048, 10240, 8192) == 4 * 2048 * (10240 - 8192) * 4
+    assert "_h" in lib.config_name(2048, 10240, 8192)
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 28672, 8192),
                     (1024, 28672, 8192), (256, 8192, 8192), (300, 520, 456)]:
         assert "_h" not in lib.config_name(M, N, K), (M, N, K)
@@ -168,17 +167,21 @@ def test_hybrid_plan_names_on_the_host(lib):
     for M in (512, 1024, 2048, 3000, 4096, 10240):
         for N in (2048, 5376, 8192, 10240, 28672):
             for K in (5376, 8192):
-                m = pat.match(lib.config_name(M, N, K))
+                name = lib.config_name(M, N, K)
+                m = pat.match(name)
                 if not m:
+                    assert "_h" not in name, name
                     continue
                 seen += 1
                 bm, bn, S = int(m.group(1)), int(m.group(2)), int(m.group(4))
                 tiles_m, tiles_n = -(-M // bm), -(-N // bn)
+                assert tiles_m * tiles_n > 256 and tiles_m * tiles_n % 256, (M, N, K)
                 head_cols = (tiles_m * tiles_n // 256) * 256 // tiles_m
-                assert 0 < head_cols < tiles_n
-                assert (tiles_n - head_cols) * tiles_m * S <= 256, (M, N, K)
-                assert lib.workspace_size(M, N, K) == S * M * (N - head_cols * bn) * 4
-    assert seen >= 10
+                assert 0 < head_cols < tiles_n and S >= 2
+                ws = lib.workspace_size(M, N, K)
+                assert ws == S * M * (N - head_cols * bn) * 4, (M, N, K, name)
+                assert ws <= lib.GEMM_NOALLOC_SCRATCH_BYTES
+    assert seen >= 5
 
     def rc(name):
         return so.gemm_bf16_ex(name.encode(), 0, 8, 8, None, 8, None, 8, fake, 8, 0, None)
@@ -187,6 +190,32 @@ def test_hybrid_plan_names_on_the_host(lib):
     assert rc(big + "_k1_g4_h0") == lib.GEMM_OK
     assert rc(big + "_k2_g4_h3") == lib.GEMM_ERR_UNSUPPORTED
     assert rc(big + "_k1_g4_P256_h2") == lib.GEMM_ERR_UNSUPPORTED
+
+
+def test_model_plans_keep_the_metric_shapes_and_fill_the_chip(lib):
+    """For M > 256 the plan is the cheapest under a fitted cost model.  It
+    keeps the measured plans of the compute-bound workload shapes, never
+    splits past 8 K-steps a slice or the no-allocation scratch, and fixes
+    the earlier rules' known losses (a 256 x 256 tile at three quarters of
+    a pass beat 1.5 passes of 256 x 128 tiles; 4 x 48 split units beat 288)."""
+    big = "t256x256x64_w2x2_s2_x3_p10"
+    assert lib.config_name(4096, 4096, 4096) == big + "_k1_g4"
+    assert lib.config_name(8192, 8192, 8192) == big + "_k1_g4"
+    assert lib.config_name(8192, 28672, 8192) == big + "_k1_g4"
+    assert lib.config_name(512, 8192, 5376) == "t128x128x64_w2x2_s4_x3_p10_k1_g4"
+    assert lib.config_name(3072, 4096, 4096) == big + "_k1_g4"
+    assert lib.config_name(768, 4096, 14336) == big + "_k4_g4"
+    plan = re.compile(r"^t(\d+)x(\d+)x(\d+)_w\dx\d_s\d+_x\d_p\d+_k(\d+)_g\d+(_h\d+)?$")
+    for M in (257, 300, 384, 640, 1000, 2500, 5000):
+        for N in (512, 3000, 4096, 11008, 14336):
+            for K in (256, 1000, 4096, 14336):
+                name = lib.config_name(M, N, K)
+                m = plan.match(name)
+                assert m, (M, N, K, name)
+                S, bk = int(m.group(4)), int(m.group(3))
+                if S > 1:
+                    assert -(-K // bk) // S >= 7, (M, N, K, name)
+                assert lib.workspace_size(M, N, K) <= lib.GEMM_NOALLOC_SCRATCH_BYTES
 
 
 def test_persistent_plan_names_on_the_host(lib):
