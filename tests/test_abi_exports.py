@@ -218,6 +218,19 @@ def test_model_plans_keep_the_metric_shapes_and_fill_the_chip(lib):
                 assert lib.workspace_size(M, N, K) <= lib.GEMM_NOALLOC_SCRATCH_BYTES
 
 
+def test_rows_of_128_tiles_for_m_up_to_128(lib):
+    """64 < M <= 128: one row of 128 x 128 tiles with K-step rotation and K
+    split to about 256 workgroups (the 256-row tiles would pad M to 256)."""
+    for M in (65, 96, 128):
+        for N, K in ((4096, 4096), (8192, 8192), (28672, 8192), (4096, 14336)):
+            name = lib.config_name(M, N, K)
+            m = re.match(r"^t128x128x64_w2x2_s4_x3_p10_k(\d+)_g4_r1$", name)
+            assert m, (M, N, K, name)
+            tiles = -(-N // 128)
+            S = int(m.group(1))
+            assert tiles * S <= 256 + tiles // 2 and -(-K // 64) // S >= 8 or S == 1, name
+
+
 def test_persistent_plan_names_on_the_host(lib):
     """Plan names with a persistent grid (_P<n>): accepted for the tile built
     with it (M = 0, so nothing is launched), refused with a split, on a tile
