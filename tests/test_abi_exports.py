@@ -315,7 +315,8 @@ def test_f16_configs(lib):
 def test_degenerate_shapes_on_the_host(lib):
     """Empty M, N or K: plan naming and workspace sizing must not fault on
     the host (a zero tile count once divided by zero here)."""
-    for M, N, K in [(0, 16, 8), (4, 0, 8), (0, 0, 0), (5, 16, 0), (1, 1, 1)]:
+    for M, N, K in [(0, 16, 8), (4, 0, 8), (0, 0, 0), (5, 16, 0), (1, 1, 1), (300, 0, 8),
+                    (300, 16, 0), (257, 1, 1), (65, 0, 0), (100000, 8, 8), (4096, 8, 100000)]:
         assert lib.config_name(M, N, K)
         assert lib.workspace_size(M, N, K) >= 0
     so = lib._lib
