@@ -1,6 +1,7 @@
 """The library inside a captured HIP graph: one gemm_bf16 call (split K with
-its reduction kernel, and an unsplit call) captured once on a stream whose
-workspace was reserved beforehand, then replayed several times with new
+its reduction kernel, an unsplit call, and a hybrid plan) captured once on a
+stream whose workspace was reserved beforehand, then replayed several times
+with new
 integer inputs copied into the captured buffers between replays, eager work
 and synchronisations in between; every replay must equal the oracle
 bit for bit.  Nothing in the path allocates, synchronises or records a
@@ -13,7 +14,10 @@ from synthetic_inputs import int_bf16
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("shape", [(256, 8192, 2048), (512, 512, 512)])
+# a split-K plan (GEMM + reduction), an unsplit one, and a hybrid plan (a
+# split launch for the last tile columns, its reduction, then the unsplit
+# launch for the rest)
+@pytest.mark.parametrize("shape", [(256, 8192, 2048), (512, 512, 512), (300, 11008, 2048)])
 def test_graph_replays_match_oracle(shape):
     import torch
 
@@ -23,6 +27,8 @@ def test_graph_replays_match_oracle(shape):
     M, N, K = shape
     plan = g.config_name(M, N, K)
     print(shape, plan, flush=True)
+    if M == 300:
+        assert "_h" in plan, plan
     s = torch.cuda.Stream()
     g.reserve_workspace(max(g.workspace_size(M, N, K), 256), s)
     dA = torch.zeros((M, K), dtype=torch.int16, device="cuda")
