@@ -1,10 +1,9 @@
 """The library inside a captured HIP graph: one gemm_bf16 call (split K with
 its reduction kernel, an unsplit call, and a hybrid plan) captured once on a
 stream whose workspace was reserved beforehand, then replayed several times
-with new
-integer inputs copied into the captured buffers between replays, eager work
-and synchronisations in between; every replay must equal the oracle
-bit for bit.  Nothing in the path allocates, synchronises or records a
+with new integer inputs copied into the captured buffers between replays,
+eager work and synchronisations in between; every replay must equal the
+oracle bit for bit.  Nothing in the path allocates, synchronises or records a
 memset, so the captured launches are the whole call."""
 import numpy as np
 import pytest
