@@ -7,7 +7,10 @@ N(0,1) inputs (``--workload`` selects another shape of
 ``synthetic_inputs.WORKLOADS``; ``--dtype f16`` measures the fp16-operand
 entry point).  The line also carries a ``workloads`` object: the M = 8192
 prefill and M = 256 decode linear layers timed the same way (same steps and
-warm-up), each with its roofline fraction.
+warm-up), each with its roofline fraction.  ``--shapes MxNxK,...`` times
+further shapes the same way (N(0,1) activations, weights scaled by
+1/sqrt(K), as the workloads) under ``shapes``; with ``--context`` every
+timed shape also carries the vendor library's time on the same tensors.
 
 Timing, per workload:
   * clock ramp: the GEMM runs untimed for ``--ramp-s`` seconds first, because
@@ -370,6 +373,8 @@ def main() -> int:
     ap.add_argument("--workloads", default="default",
                     help="the shapes of the 'workloads' object: 'default' (the prefill and "
                          "decode layers), 'none', or a comma list of workload names")
+    ap.add_argument("--shapes", default="",
+                    help="extra shapes MxNxK,MxNxK timed like the workloads, under 'shapes'")
     ap.add_argument("--config", default=None, help="force a kernel configuration")
     ap.add_argument("--hot", action="store_true",
                     help="reuse one B for memory-bound shapes too (B may stay in cache)")
@@ -395,7 +400,7 @@ def main() -> int:
     import torch
 
     import dense_gemm_bf16_amd as g
-    from synthetic_inputs import WORKLOADS
+    from synthetic_inputs import WORKLOADS, Workload
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -473,6 +478,17 @@ def main() -> int:
             torch.cuda.empty_cache()
             wl[name] = res
         out["workloads"] = wl
+
+    if args.shapes:
+        sh = {}
+        for spec in (x for x in args.shapes.split(",") if x):
+            Ms, Ns, Ks = (int(v) for v in spec.split("x"))
+            ws = Workload(spec, Ms, Ns, Ks, "normal", True, 0x5A01, 0x5B01)
+            res, keep = time_workload(g, torch, np, ws, args, stream, clocks)
+            del keep
+            torch.cuda.empty_cache()
+            sh[spec] = res
+        out["shapes"] = sh
 
     if args.context:
         out["context"] = {"vendor": head["vendor"]}

@@ -25,7 +25,9 @@ Usage::
 
 ``fit`` reads ``plan_model_data/fit_shapes.json`` (77 shapes, 1,000 plan
 timings on MI355X) and reports the choice quality on
-``plan_model_data/holdout_shapes.json`` (42 other shapes).
+``plan_model_data/holdout_shapes.json`` (42 other shapes) and
+``plan_model_data/multipass_shapes.json`` (30 shapes of up to 8.75 passes
+of 256 x 256 tiles over the CUs, swept with this module).
 """
 from __future__ import annotations
 
@@ -254,7 +256,9 @@ def main(argv=None) -> int:
     sw.add_argument("--out", required=True)
     ft = sub.add_parser("fit", help="fit the constants and report the choice quality")
     ft.add_argument("--data", default=os.path.join(DATA, "fit_shapes.json"))
-    ft.add_argument("--holdout", default=os.path.join(DATA, "holdout_shapes.json"))
+    ft.add_argument("--holdout", default=",".join(
+        os.path.join(DATA, f) for f in ("holdout_shapes.json", "multipass_shapes.json")),
+        help="comma list of sweeps to report the choice quality on")
     args = ap.parse_args(argv)
     if args.cmd == "sweep":
         Ms = [int(x) for x in args.ms.split(",")]
@@ -267,7 +271,8 @@ def main(argv=None) -> int:
     print(f"{len(rows_of(data))} timings of {len(data)} shapes; RMS log error {rms:.4f}")
     for name, v in zip(NAMES, p):
         print(f"  {name:18s} {v:.4f}")
-    for label, path in (("fit shapes", args.data), ("held-out shapes", args.holdout)):
+    for label, path in [("fit shapes", args.data)] + [
+            (f"held out ({os.path.basename(h)})", h) for h in args.holdout.split(",") if h]:
         with open(path) as f:
             q = choice_quality(p, json.load(f))
         print(f"{label}: model's pick / fastest timed {geomean(v[0] for v in q.values()):.4f} "
