@@ -233,7 +233,8 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
 // tile unsplit, split 2-8 and hybrid.  RMS error 4.5 %; on 42 other shapes
 // (M 288-5120, N x K with N or K of 3072-16384) its choice ran within 0.1 %
 // of the fastest plan timed (geometric mean; 3.5 % at worst), against 7.2 %
-// (and up to 50 %) for the earlier rules.
+// (and up to 50 %) for the earlier rules.  dense_gemm_bf16_amd/plan_model.py
+// holds the same model, the sweep and the fit, with the measurements.
 //
 // A launch of `tiles` tiles split S ways runs units = tiles * S workgroups,
 // one per CU at a time: each pass over the 256 CUs costs a unit's time,
@@ -253,6 +254,12 @@ constexpr double kPartialPass = 0.6767;
 constexpr double kLaunchUs = 1.1184;
 constexpr double kSplitUs = 1.4115;
 constexpr double kSplitUsPerMB = 0.3239;  // per MB of partial slices
+// A hybrid whose unsplit part makes two or more whole passes is taken only
+// if its estimate is 3 % below the others': after whole passes a partial
+// last pass runs faster than the partial-pass term says, and without the
+// margin the model preferred hybrids up to 4.7 % slower on a sweep of 30
+// such shapes (with it: 1.6 % at worst).
+constexpr double kHybridMargin = 0.03;
 constexpr int64_t kModelMinM = 257;
 
 // K splits as finish_plan equalises them: ceil(k_tiles / S) steps a slice.
@@ -312,9 +319,9 @@ Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
         const int64_t hs = even_splits(h, kt);
         if (hs <= 1) continue;
         if ((size_t)(hs * M * partial_ld(N - n1) * 4) > GEMM_NOALLOC_SCRATCH_BYTES) continue;
-        consider(t, 1, hs,
-                 launch_cost(c, tm * head_cols, 1, kt, M, n1) +
-                     launch_cost(c, tm * (tn - head_cols), hs, kt, M, N - n1));
+        const double est = launch_cost(c, tm * head_cols, 1, kt, M, n1) +
+                           launch_cost(c, tm * (tn - head_cols), hs, kt, M, N - n1);
+        consider(t, 1, hs, tm * head_cols / kCUs >= 2 ? est * (1 + kHybridMargin) : est);
       }
     }
   }
