@@ -113,7 +113,7 @@ int gemm_bf16_ex(const char* config,
                  void* C, int64_t ldc,
                  int out_f32, void* stream);
 
-/* Name of the configuration gemm_bf16 (and gemm_f16: the shape rules are the
+/* Name of the configuration gemm_bf16 (and gemm_f16: the plan choice is the
  * same for both operand types) would choose for this shape, e.g.
  * "t256x256x64_w2x2_s2_x3_p10_k1_g4": tile BM x BN x BK, waves, ring stages,
  * LDS swizzle, load schedule, then K splits and GROUP_M (and "_r<n>", the
