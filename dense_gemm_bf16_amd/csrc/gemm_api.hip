@@ -270,6 +270,12 @@ int64_t even_splits(int64_t S, int64_t k_tiles) {
   return (k_tiles + per - 1) / per;
 }
 
+// Bytes of fp32 partial slices, in floating point: the product can exceed
+// 64 bits for shapes that are only named, never run.
+double partial_bytes(int64_t S, int64_t M, int64_t N) {
+  return (double)S * (double)M * (double)partial_ld(N) * 4.0;
+}
+
 double launch_cost(const TileCost& c, int64_t tiles, int64_t S, int64_t k_tiles, int64_t M,
                    int64_t N) {
   const int64_t units = tiles * S;
@@ -277,7 +283,7 @@ double launch_cost(const TileCost& c, int64_t tiles, int64_t S, int64_t k_tiles,
   double passes = (double)(units / kCUs);
   if (units % kCUs) passes += kPartialPass + (1 - kPartialPass) * (double)(units % kCUs) / kCUs;
   double t = (steps * c.step_us + c.tile_us) * passes + kLaunchUs;
-  if (S > 1) t += kSplitUs + kSplitUsPerMB * (double)(S * M * partial_ld(N) * 4) * 1e-6;
+  if (S > 1) t += kSplitUs + kSplitUsPerMB * partial_bytes(S, M, N) * 1e-6;
   return t;
 }
 
@@ -308,7 +314,7 @@ Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
       if (S > 1 && (kt / S < 8 || tiles * S > 4 * kCUs)) continue;
       const int64_t s = even_splits(S, kt);
       if (S > 1 && s <= 1) continue;
-      if (s > 1 && (size_t)(s * M * partial_ld(N) * 4) > GEMM_NOALLOC_SCRATCH_BYTES) continue;
+      if (s > 1 && partial_bytes(s, M, N) > (double)GEMM_NOALLOC_SCRATCH_BYTES) continue;
       consider(t, s, 0, launch_cost(c, tiles, s, kt, M, N));
     }
     if (tiles > kCUs && tiles % kCUs) {
@@ -318,7 +324,7 @@ Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
       for (int64_t h : {2, 3, 4, 6, 8}) {
         const int64_t hs = even_splits(h, kt);
         if (hs <= 1) continue;
-        if ((size_t)(hs * M * partial_ld(N - n1) * 4) > GEMM_NOALLOC_SCRATCH_BYTES) continue;
+        if (partial_bytes(hs, M, N - n1) > (double)GEMM_NOALLOC_SCRATCH_BYTES) continue;
         const double est = launch_cost(c, tm * head_cols, 1, kt, M, n1) +
                            launch_cost(c, tm * (tn - head_cols), hs, kt, M, N - n1);
         consider(t, 1, hs, tm * head_cols / kCUs >= 2 ? est * (1 + kHybridMargin) : est);
@@ -341,6 +347,16 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
   Plan p{};
   p.group_m = 4;
   const TileConfig* big = find_tile_config(kBig);
+  constexpr int64_t kMaxDim = int64_t(1) << 31;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) {
+    // Beyond the kernels' 32-bit shape fields (such calls are refused): a
+    // name only, computed without the tile and byte counts below, which
+    // could overflow for such sizes.
+    p.tile = big;
+    p.splits = 1;
+    snprintf(p.name, sizeof p.name, "%s_k1_g4", big->name);
+    return p;
+  }
   const int64_t big_tiles = tiles_of(big, M, N);
   if (M >= kModelMinM) {
     Plan m = model_plan(M, N, K, half);

@@ -313,10 +313,13 @@ def test_f16_configs(lib):
 
 
 def test_degenerate_shapes_on_the_host(lib):
-    """Empty M, N or K: plan naming and workspace sizing must not fault on
-    the host (a zero tile count once divided by zero here)."""
+    """Empty M, N or K, and sizes beyond what any kernel runs: plan naming and
+    workspace sizing must not fault on the host (a zero tile count once
+    divided by zero here)."""
     for M, N, K in [(0, 16, 8), (4, 0, 8), (0, 0, 0), (5, 16, 0), (1, 1, 1), (300, 0, 8),
-                    (300, 16, 0), (257, 1, 1), (65, 0, 0), (100000, 8, 8), (4096, 8, 100000)]:
+                    (300, 16, 0), (257, 1, 1), (65, 0, 0), (100000, 8, 8), (4096, 8, 100000),
+                    (1 << 31, 8, 8), (1 << 62, 1 << 62, 1 << 62), ((1 << 31) - 1, (1 << 31) - 1,
+                                                                    (1 << 31) - 1)]:
         assert lib.config_name(M, N, K)
         assert lib.workspace_size(M, N, K) >= 0
     so = lib._lib
