@@ -4,8 +4,8 @@ Each ``csrc/*.hip`` file is compiled to an object in parallel with hipcc,
 then linked into a shared library next to this file.  Build products live in
 ``_build/`` (ignored by git) and the package directory.
 
-The default build holds the product configurations (those the shape rules
-and the tuned table choose).  ``build(ablation=True)``, or the environment
+The default build holds the product configurations (those the plan choice
+-- tuned table, cost model, rules -- can pick).  ``build(ablation=True)``, or the environment
 variable ``GEMM_BUILD_ABLATION=1``, also compiles ``csrc/ablation/``: the
 kernel families and LDS layouts the product choices were measured against,
 selectable by name through ``gemm_bf16_ex`` for ablations and sweeps.

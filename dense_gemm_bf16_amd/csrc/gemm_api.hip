@@ -149,7 +149,8 @@ constexpr const char* kSkinny32 = "t32x128x64_w1x4_s6_x2_p0";
 constexpr const char* kSkinny64 = "t64x128x64_w1x4_s6_x2_p0";
 
 // Shapes measured by the offline tuning sweep (dense_gemm_bf16_amd/tune.py):
-// exact (M, N, K) -> plan name, consulted before the rules below.
+// exact (M, N, K) -> plan name, consulted before the cost model and the
+// rules below.
 struct TunedPlan {
   int64_t M, N, K;
   const char* plan;

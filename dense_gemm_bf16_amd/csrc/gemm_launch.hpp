@@ -170,8 +170,8 @@ hipError_t launch_cfg(const KernelArgs& a, int grid, hipStream_t s, int flags) {
 // several translation units) takes them from a GEMM_*_PARAMS macro, through
 // GEMM_ROW so the macro expands into separate arguments.
 //
-// The product set is every configuration the shape rules or the tuned
-// table can choose:
+// The product set is every configuration the plan choice (tuned table,
+// cost model, rules) can pick:
 //   big     256 x 256 direct-to-LDS, 16x16x32 MFMAs (4096^3, prefill)
 //   mid     256 x 128 direct-to-LDS, three ring slots (M = 256 decode)
 //   mid128  128 x 128 direct-to-LDS, four ring slots (M = 512 class)

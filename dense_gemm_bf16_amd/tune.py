@@ -197,7 +197,7 @@ def choose_entries(results: dict, old: dict, min_gain: float) -> list[tuple[int,
     is that table entry, not the static rules.  So: a shape gets the sweep's
     best plan if it beats the current choice by more than min_gain; else a
     shape already in the table keeps its entry (still within min_gain of the
-    best); else the rules stay in charge."""
+    best); else the automatic choice (cost model or rules) stays in charge."""
     entries = []
     for key, r in results.items():
         M, N, K = (int(v) for v in key.split("x"))
@@ -215,8 +215,9 @@ def write_table(entries: list[tuple[int, int, int, str]], path: str, note: str) 
     lines = [
         "// Shape -> launch plan table written by dense_gemm_bf16_amd/tune.py.",
         f"// {note}.",
-        "// Exact (M, N, K) matches only; other shapes use the rules in",
-        "// gemm_api.hip.  Regenerate with the tuning sweep, do not edit by hand.",
+        "// Exact (M, N, K) matches only; other shapes use the automatic choice",
+        "// in gemm_api.hip (cost model, rules).  Regenerate with the tuning sweep,",
+        "// do not edit by hand.",
     ]
     for M, N, K, plan in entries:
         lines.append(f'{{{M}, {N}, {K}, "{plan}"}},')
