@@ -225,7 +225,10 @@ def sweep(Ms, NKs, out_path: str) -> None:
     torch.cuda.set_device(0)
     s = torch.cuda.current_stream()
     g.reserve_workspace(1 << 30, s)
-    maxM, maxN, maxK = max(Ms), max(n for n, _ in NKs), max(k for _, k in NKs)
+    def ld(x):  # row strides are multiples of 8 elements
+        return -(-x // 8) * 8
+
+    maxM, maxN, maxK = max(Ms), ld(max(n for n, _ in NKs)), ld(max(k for _, k in NKs))
     A = torch.randn(maxM * maxK, device="cuda").to(torch.bfloat16)
     B = torch.randn(maxN * maxK, device="cuda").to(torch.bfloat16)
     C = torch.empty(maxM * maxN, device="cuda", dtype=torch.bfloat16)
@@ -233,8 +236,9 @@ def sweep(Ms, NKs, out_path: str) -> None:
     for N, K in NKs:
         for M in Ms:
             def run(plan):
-                rc = g._lib.gemm_bf16_ex(plan.encode(), M, N, K, A.data_ptr(), K, B.data_ptr(),
-                                         K, C.data_ptr(), N, 0, ctypes.c_void_p(s.cuda_stream))
+                rc = g._lib.gemm_bf16_ex(plan.encode(), M, N, K, A.data_ptr(), ld(K),
+                                         B.data_ptr(), ld(K), C.data_ptr(), ld(N), 0,
+                                         ctypes.c_void_p(s.cuda_stream))
                 if rc:
                     raise RuntimeError(f"{plan}: status {rc}")
             auto = g.config_name(M, N, K)
