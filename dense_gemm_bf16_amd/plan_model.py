@@ -28,7 +28,9 @@ Usage::
 timings on MI355X) and reports the choice quality on
 ``plan_model_data/holdout_shapes.json`` (42 other shapes) and
 ``plan_model_data/multipass_shapes.json`` (30 shapes of up to 8.75 passes
-of 256 x 256 tiles over the CUs, swept with this module).
+of 256 x 256 tiles over the CUs) and ``plan_model_data/irregular_shapes.json``
+(20 shapes with M, N and K off the tile sizes, rows off 128-byte lines),
+both swept with this module.
 """
 from __future__ import annotations
 
@@ -279,7 +281,8 @@ def main(argv=None) -> int:
     ft = sub.add_parser("fit", help="fit the constants and report the choice quality")
     ft.add_argument("--data", default=os.path.join(DATA, "fit_shapes.json"))
     ft.add_argument("--holdout", default=",".join(
-        os.path.join(DATA, f) for f in ("holdout_shapes.json", "multipass_shapes.json")),
+        os.path.join(DATA, f) for f in ("holdout_shapes.json", "multipass_shapes.json",
+                                        "irregular_shapes.json")),
         help="comma list of sweeps to report the choice quality on")
     args = ap.parse_args(argv)
     if args.cmd == "sweep":
