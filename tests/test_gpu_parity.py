@@ -341,6 +341,57 @@ def test_random_shapes_automatic_plan_bit_exact():
     print("tiles used:", sorted(plans), flush=True)
 
 
+def test_random_named_plans_bit_exact():
+    """Thirty seeded random (plan, shape) pairs: a product tile, K split 1-4,
+    K-step rotation on or off, non-temporal B on the tiles built with it,
+    GROUP_M 4 or 8, M, N and K random and mostly ragged, A and B row strides
+    padded by a random multiple of 8 elements (NaN in the padding), fp32
+    output for one call in three; integer inputs, so every result is exact.
+    Hybrid plans are named where the shape gives them a tail (three row tiles
+    over a long N)."""
+    import dense_gemm_bf16_amd as g
+
+    rng = np.random.default_rng(5151)
+    o = _oracle()
+    tiles = sorted(PRODUCT_CONFIGS)
+    stream = set(STREAM_TILES)
+    for i in range(30):
+        tile = tiles[int(rng.integers(len(tiles)))]
+        bm, bn = int(tile[1:].split("x")[0]), int(tile.split("x")[1])
+        hybrid = bm >= 128 and i % 5 == 0
+        if hybrid:  # 3 rows of tiles x 90 columns: more than one pass of 256
+            M = 2 * bm + int(rng.integers(1, bm))
+            N = 89 * bn + int(rng.integers(1, bn))
+            K = int(rng.integers(130, 400))
+        else:
+            M = int(rng.integers(1, 3 * bm + 1))
+            N = int(rng.integers(1, 2000))
+            K = int(rng.integers(1, 700))
+        S = 1 if hybrid else int(rng.integers(1, 5))
+        name = f"{tile}_k{S}_g{int(rng.choice([4, 8]))}"
+        if rng.random() < 0.5:
+            name += "_r1"
+        if tile in stream and rng.random() < 0.5:
+            name += "_n1"
+        if hybrid:
+            name += f"_h{int(rng.integers(2, 5))}"
+        pad_a, pad_b = 8 * int(rng.integers(0, 3)), 8 * int(rng.integers(0, 3))
+        kk = (K + 7) // 8 * 8
+        A = np.full((M, kk + pad_a), 0x7FC0, np.uint16)
+        B = np.full((N, kk + pad_b), 0x7FC0, np.uint16)
+        A[:, :K] = int_bf16(M, K, seed=1600 + 2 * i)
+        B[:, :K] = int_bf16(N, K, seed=1601 + 2 * i)
+        ref16, ref64 = o.gemm(A, B, K=K)
+        f32 = i % 3 == 0
+        got = run_gemm(A, B, K=K, config=name, out_f32=f32)
+        if f32:
+            rep = check_f32(got, ref64, K, exact=True)
+        else:
+            rep = check_bf16(got, ref16, None, K, exact=True)
+        print(i, name, (M, N, K), "f32" if f32 else "bf16", rep, flush=True)
+        assert rep["ok"], (name, (M, N, K), rep)
+
+
 PRODUCT_CONFIGS = {
     "t256x256x64_w2x2_s2_x3_p10", "t256x128x64_w2x2_s3_x3_p10", "t128x128x64_w2x2_s4_x3_p10",
     "t32x32x64_w1x1_s8_x2_p9", "t64x32x64_w1x1_s6_x2_p9", "t64x128x64_w1x4_s6_x2_p0",
