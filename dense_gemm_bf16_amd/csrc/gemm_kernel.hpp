@@ -713,11 +713,14 @@ struct LdsStage {
 // back (measured 0.7-2 % faster at 4096^3 and 8192^3, where C would
 // otherwise evict A and B panels from L2).  Split-K partials are stored
 // normally, since the reduction reads them right after (non-temporal, their
-// calls were ~1 % slower).
-template <typename Cfg, int OUT, int LIMIT = Cfg::kLdsBytes, bool NT = false>
+// calls were ~1 % slower).  EDGE (a tile that C's last row or column cuts):
+// rows at or past M are skipped, a 16-byte piece wholly inside N is stored
+// whole, the one that N cuts element by element, pieces past N not at all.
+template <typename Cfg, int OUT, int LIMIT = Cfg::kLdsBytes, bool NT = false, bool EDGE = false>
 __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int64_t ld,
                                                const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                               int m_base, int n_base, int lane) {
+                                               int m_base, int n_base, int lane, int M = 0,
+                                               int N = 0) {
   using St = LdsStage<Cfg, OUT, LIMIT>;
   static_assert(St::kOk, "staging fits the ring");
   constexpr int kE = St::kE, kRB = St::kRB, MF = Cfg::kMf;
@@ -758,6 +761,23 @@ __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int6
       if constexpr (St::kSwapHalves)
         if (((j * RPI) & 16) != 0) v = (u32x4){v[2], v[3], v[0], v[1]};
       u32x4* const dst = (u32x4*)(out + (int64_t)((pass * St::kPassRows + j * RPI) * kE) * ld);
+      if constexpr (EDGE) {
+        constexpr int kPer = 16 / kE;  // elements in a 16-byte piece
+        const int row = m_base + pass * St::kPassRows + j * RPI + rr;
+        const int col = n_base + rc * kPer;
+        if (row >= M || col >= N) continue;
+        if (col + kPer > N) {
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            if (col + e >= N) break;
+            if constexpr (kE == 4)
+              ((uint32_t*)dst)[e] = v[e];
+            else
+              ((uint16_t*)dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          }
+          continue;
+        }
+      }
       if constexpr (NT)
         __builtin_nontemporal_store(v, dst);
       else
@@ -768,9 +788,10 @@ __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int6
 
 // The epilogue of every kernel: C (OUT), or with SPLIT the K-slice's
 // unrounded fp32 sums into its partial buffer (the reduction kernel in
-// gemm_reduce.hip adds the slices in a fixed order), through LDS for tiles
-// wholly inside C when the staging fits the ring, else straight from the
-// accumulators.  Called by all waves of the workgroup after the main loop
+// gemm_reduce.hip adds the slices in a fixed order), through LDS when the
+// staging fits the ring (tiles that C's last row or column cuts with the
+// stores predicated: element by element from the accumulators, they cost
+// 3-4.5 % of a 4096^3-class call), else straight from the accumulators.  Called by all waves of the workgroup after the main loop
 // (the LDS path has a barrier); the ring must not be written again.
 // (An in-kernel reduction by the last slice to finish a tile was measured
 // 2-3x slower: making the partials visible to the other XCDs needs a
@@ -784,14 +805,16 @@ __device__ __forceinline__ void finish_tile(const KernelArgs& a, lds_u8* smem, i
   void* const base = SPLIT ? (void*)(a.part + (int64_t)split * a.part_stride) : a.C;
   const int64_t ld = SPLIT ? a.ldp : a.ldc;
   if constexpr (St::kOk) {
-    if (m0 + Cfg::kBM <= a.M && n0 + Cfg::kBN <= a.N) {
-      // every wave is done with the ring: loads landed, fragments read
-      // (kBarrier false: the caller has made sure of it)
-      if constexpr (kBarrier) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // every wave is done with the ring: loads landed, fragments read
+    // (kBarrier false: the caller has made sure of it)
+    if constexpr (kBarrier) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (m0 + Cfg::kBM <= a.M && n0 + Cfg::kBN <= a.N)
       store_tile_lds<Cfg, kOut, LIMIT, !SPLIT>(smem + wave * St::kWaveBytes, base, ld, acc,
                                                m_base, n_base, lane);
-      return;
-    }
+    else
+      store_tile_lds<Cfg, kOut, LIMIT, !SPLIT, true>(smem + wave * St::kWaveBytes, base, ld,
+                                                     acc, m_base, n_base, lane, a.M, a.N);
+    return;
   }
   store_tile<Cfg, kOut>(a, base, ld, acc, m_base, n_base, lane);
 }

@@ -28,10 +28,12 @@
  *
  * Alignment (required): A, B and C 16-byte aligned; lda, ldb and ldc
  * multiples of 8 elements.  Otherwise GEMM_ERR_MISALIGNED.  (Recommended:
- * A and B 128-byte aligned with lda and ldb multiples of 64 elements, so
- * that every 128-byte piece of a row lies in one cache line; with rows that
- * start off a line, e.g. lda = ldb = K = 8168 or 7000, a compute-bound call
- * ran 10-12 % slower than with the rows padded to 8192 or 7040.)
+ * A, B and C 128-byte aligned with lda, ldb and ldc multiples of 64
+ * elements, so that every 128-byte piece of a row lies in one cache line;
+ * with rows that start off a line, e.g. lda = ldb = K = 8168 or 7000, a
+ * compute-bound call ran 10-12 % slower than with the rows padded to 8192
+ * or 7040, and 4096 x 4088 x 4096 2 % slower with ldc = 4088 than with
+ * ldc = 4096.)
  *
  * Numerics.  Products of bf16 values are exact in fp32; sums are fp32 in an
  * order fixed by the chosen configuration (so results are bitwise
