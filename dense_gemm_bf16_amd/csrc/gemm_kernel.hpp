@@ -723,6 +723,9 @@ __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int6
                                                int N = 0) {
   using St = LdsStage<Cfg, OUT, LIMIT>;
   static_assert(St::kOk, "staging fits the ring");
+  // the lane index again from the hardware rather than kept live through the
+  // main loop (kept, it spilled to scratch in the 256 x 256 kernel)
+  lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   constexpr int kE = St::kE, kRB = St::kRB, MF = Cfg::kMf;
   constexpr int LPR = kRB / 16;  // lanes per row when reading back
   constexpr int RPI = 64 / LPR;  // rows per read instruction (divides 16)
