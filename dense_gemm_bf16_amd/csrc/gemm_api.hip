@@ -411,7 +411,11 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
     } else {
       p.tile = m128;
       p.splits = choose_splits(tiles_of(m128, M, N), k_tiles);
-      p.k_rot = 0;
+      // Two rows of tiles: rotation when each workgroup runs 32 K-steps or
+      // more.  Interleaved, B cold, M = 160-256: 2.0-4.4 % faster on the 12
+      // such shapes (N or K 11008-14336), 0.5-5 % slower on the 12 with
+      // 16-27 steps (4096 x 4096, 5120 x 5120, 6144 x 4096).
+      p.k_rot = (M + m128->bm - 1) / m128->bm <= 2 && k_tiles / p.splits >= 32 ? 1 : 0;
     }
   }
   if (M > 64 && p.splits == 1) {

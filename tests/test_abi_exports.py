@@ -231,6 +231,23 @@ def test_rows_of_128_tiles_for_m_up_to_128(lib):
             assert tiles * S <= 256 + tiles // 2 and -(-K // 64) // S >= 8 or S == 1, name
 
 
+def test_two_rows_of_128_tiles_rotate_on_long_k_loops(lib):
+    """128 < M <= 256 on 128 x 128 tiles (two rows): K-step rotation exactly
+    when each workgroup runs at least 32 K-steps."""
+    seen = set()
+    for M in (160, 192, 224, 256):
+        for N, K in ((4096, 4096), (5120, 5120), (6144, 4096), (11008, 4096),
+                     (14336, 4096), (4096, 11008)):
+            name = lib.config_name(M, N, K)
+            m = re.match(r"^t128x128x64_w2x2_s4_x3_p10_k(\d+)_g4(_r1)?$", name)
+            if not m:
+                continue
+            steps = -(-K // 64) // int(m.group(1))
+            assert bool(m.group(2)) == (steps >= 32), (M, N, K, name)
+            seen.add(steps >= 32)
+    assert seen == {True, False}
+
+
 def test_persistent_plan_names_on_the_host(lib):
     """Plan names with a persistent grid (_P<n>): accepted for the tile built
     with it (M = 0, so nothing is launched), refused with a split, on a tile
