@@ -40,10 +40,10 @@
 // Each load keeps its own per-lane offset register (row*ld*2 + chunk*16, or
 // an out-of-range value for rows past M or N, which then read zero), so the
 // issue of a load is one M0 update and the instruction; the K offset of the
-// step goes in the (unchecked) scalar offset.  A step that reaches past K
-// (compiled only when K % BK != 0) moves the K offset into the range-checked
-// per-lane offset instead and sends chunks at or past K out of range; a
-// chunk that straddles K (K % 8 != 0) is trimmed in LDS once it has landed.
+// step goes in the (unchecked) scalar offset.  In the step that K ends in
+// (compiled only when K % BK != 0) the lanes whose chunk starts at or past K
+// take the out-of-range offset instead (a select, not a branch); a chunk
+// that straddles K (K % 8 != 0) is trimmed in LDS once it has landed.
 #pragma once
 
 #include "gemm_kernel.hpp"

@@ -669,11 +669,11 @@ __device__ __forceinline__ void store_tile(const KernelArgs& a, void* Cbase, int
 // Stored straight from the accumulators, one store instruction writes 8 or
 // 16 bytes into each of 32 rows (a lane holds 4 consecutive columns of one
 // row), and the L2 takes one partial-line write per row and instruction: on
-// MI355X that made the 256 x 256 tile's bf16 epilogue take 8-10 us.  When
-// the LDS ring is idle (after the main loop) and the tile lies wholly
-// inside C, the waves instead write their accumulator blocks into LDS and
-// read them back by rows, so that 16 consecutive lanes store 256 contiguous
-// bytes of one row (whole 128-byte lines).
+// MI355X that made the 256 x 256 tile's bf16 epilogue take 8-10 us.  Once
+// the LDS ring is idle (after the main loop), the waves instead write their
+// accumulator blocks into LDS and read them back by rows, so that 16
+// consecutive lanes store 256 contiguous bytes of one row (whole 128-byte
+// lines).
 //
 // Staging layout, per wave: row r of the wave block (kRB bytes) holds
 // 16-byte chunk c at r*kRB + 16 (c ^ sw(r)), sw(r) = r % 16, or (r / 2) % 8
@@ -719,13 +719,12 @@ struct LdsStage {
 template <typename Cfg, int OUT, int LIMIT = Cfg::kLdsBytes, bool NT = false, bool EDGE = false>
 __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int64_t ld,
                                                const typename Cfg::Acc (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                               int m_base, int n_base, int lane, int M = 0,
-                                               int N = 0) {
+                                               int m_base, int n_base, int M = 0, int N = 0) {
   using St = LdsStage<Cfg, OUT, LIMIT>;
   static_assert(St::kOk, "staging fits the ring");
-  // the lane index again from the hardware rather than kept live through the
-  // main loop (kept, it spilled to scratch in the 256 x 256 kernel)
-  lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  // the lane index from the hardware rather than kept live through the main
+  // loop (kept, it spilled to scratch in the 256 x 256 kernel)
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   constexpr int kE = St::kE, kRB = St::kRB, MF = Cfg::kMf;
   constexpr int LPR = kRB / 16;  // lanes per row when reading back
   constexpr int RPI = 64 / LPR;  // rows per read instruction (divides 16)
@@ -792,10 +791,12 @@ __device__ __forceinline__ void store_tile_lds(lds_u8* region, void* Cbase, int6
 // The epilogue of every kernel: C (OUT), or with SPLIT the K-slice's
 // unrounded fp32 sums into its partial buffer (the reduction kernel in
 // gemm_reduce.hip adds the slices in a fixed order), through LDS when the
-// staging fits the ring (tiles that C's last row or column cuts with the
-// stores predicated: element by element from the accumulators, they cost
-// 3-4.5 % of a 4096^3-class call), else straight from the accumulators.  Called by all waves of the workgroup after the main loop
-// (the LDS path has a barrier); the ring must not be written again.
+// staging fits the ring, also for the tiles that C's last row or column
+// cuts (their row pieces predicated; stored element by element from the
+// accumulators instead, such tiles cost 3-4.5 % of a 4096^3-class call),
+// else straight from the accumulators.  Called by all waves of the
+// workgroup after the main loop (the LDS path has a barrier); the ring must
+// not be written again.
 // (An in-kernel reduction by the last slice to finish a tile was measured
 // 2-3x slower: making the partials visible to the other XCDs needs a
 // release fence per workgroup, which writes back that XCD's L2.)
@@ -813,10 +814,10 @@ __device__ __forceinline__ void finish_tile(const KernelArgs& a, lds_u8* smem, i
     if constexpr (kBarrier) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (m0 + Cfg::kBM <= a.M && n0 + Cfg::kBN <= a.N)
       store_tile_lds<Cfg, kOut, LIMIT, !SPLIT>(smem + wave * St::kWaveBytes, base, ld, acc,
-                                               m_base, n_base, lane);
+                                               m_base, n_base);
     else
       store_tile_lds<Cfg, kOut, LIMIT, !SPLIT, true>(smem + wave * St::kWaveBytes, base, ld,
-                                                     acc, m_base, n_base, lane, a.M, a.N);
+                                                     acc, m_base, n_base, a.M, a.N);
     return;
   }
   store_tile<Cfg, kOut>(a, base, ld, acc, m_base, n_base, lane);
