@@ -392,7 +392,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus "
               f"{args.gpus}); nothing was run.", file=sys.stderr)
         return 2
 

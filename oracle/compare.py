@@ -61,7 +61,7 @@ def abs_floor(K: int, sigma_a: float = 1.0, sigma_b: float = 1.0) -> float:
 def check_bf16(got_bits, ref_bits, ref_sum, K, sigma_a=1.0, sigma_b=1.0,
                exact=False, fmt="bf16") -> dict:
     """Compare GPU 16-bit results (bf16, or fp16 with ``fmt="f16"``) with the
-    oracle.  Returns a report dict whose ``ok`` field is the verdict."""
+    oracle.  Returns a report dict whose ``ok`` field is the outcome."""
     got_bits = np.asarray(got_bits, np.uint16)
     ref_bits = np.asarray(ref_bits, np.uint16)
     d = ulp_dist(got_bits, ref_bits)
