@@ -652,3 +652,22 @@ def test_automatic_hybrid_plan_on_a_qkv_shape():
     rep = check_bf16(got[:, cols], c16, c64, K, 1.0, K ** -0.5)
     print("cols", rep, flush=True)
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("M,N,K,rot", [(200, 11008, 4096, True), (224, 4096, 11008, True),
+                                       (192, 4096, 4096, False)])
+def test_two_rows_of_128_tiles_automatic_plan(M, N, K, rot):
+    """128 < M <= 256 on two rows of 128 x 128 tiles: the automatic plan
+    rotates the K order exactly on long K loops; either way every element
+    is bit-exact on integers (full check)."""
+    import dense_gemm_bf16_amd as g
+
+    plan = g.config_name(M, N, K)
+    print("plan", plan, flush=True)
+    assert plan.startswith("t128x128") and ("_r1" in plan) == rot, plan
+    A = int_bf16(M, K, seed=1600 + M)
+    B = int_bf16(N, K, seed=1601 + M)
+    ref16, _ = _oracle().gemm(A, B)
+    rep = check_bf16(run_gemm(A, B), ref16, None, K, exact=True)
+    print(rep, flush=True)
+    assert rep["ok"], rep
