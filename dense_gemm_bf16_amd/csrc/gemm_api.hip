@@ -83,8 +83,10 @@ int64_t partial_ld(int64_t N) { return (N + 7) / 8 * 8; }
 
 
 size_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
-  if (p.split_n > 0)  // hybrid: only the columns past split_n are split
+  if (p.split_n > 0) {  // hybrid: only the columns past split_n are split
+    if (p.tail_splits <= 1) return 0;  // mixed: nothing is split
     return (size_t)p.tail_splits * (size_t)M * (size_t)partial_ld(N - p.split_n) * 4;
+  }
   if (p.splits <= 1) return 0;
   return (size_t)p.splits * (size_t)M * (size_t)partial_ld(N) * 4;
 }
@@ -213,6 +215,20 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
     }
   }
   if (p->split_n == 0) p->tail_splits = 0;
+  // Mixed: the same head as the hybrid, the columns after it unsplit on
+  // tail_tile (only 256 x 256 over 256 x 128, unsplit, no persistent grid,
+  // no non-temporal B); otherwise the plain plan.
+  if (p->tail_tile) {
+    const int64_t tiles_m = (M + p->tile->bm - 1) / p->tile->bm;
+    const int64_t tiles_n = (N + p->tile->bn - 1) / p->tile->bn;
+    const int64_t head_cols = tiles_m > 0 ? (tiles_m * tiles_n / kCUs) * kCUs / tiles_m : 0;
+    const bool ok = p->split_n == 0 && p->splits == 1 && p->persist == 0 && p->stream_b == 0 &&
+                    p->tile == find_tile_config(kBig) && p->tail_tile == find_tile_config(kMid);
+    if (ok && head_cols > 0 && head_cols < tiles_n)
+      p->split_n = head_cols * p->tile->bn;
+    else
+      p->tail_tile = nullptr;
+  }
   int n = snprintf(p->name, sizeof p->name, "%s_k%d_g%d", p->tile->name, p->splits, p->group_m);
   if (p->k_rot > 0 && n > 0 && n < (int)sizeof p->name)
     n += snprintf(p->name + n, sizeof p->name - n, "_r%d", p->k_rot);
@@ -220,8 +236,10 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
     n += snprintf(p->name + n, sizeof p->name - n, "_P%d", p->persist);
   if (p->stream_b > 0 && n > 0 && n < (int)sizeof p->name)
     n += snprintf(p->name + n, sizeof p->name - n, "_n1");
-  if (p->split_n > 0 && n > 0 && n < (int)sizeof p->name)
+  if (p->split_n > 0 && !p->tail_tile && n > 0 && n < (int)sizeof p->name)
     snprintf(p->name + n, sizeof p->name - n, "_h%d", p->tail_splits);
+  if (p->tail_tile && n > 0 && n < (int)sizeof p->name)
+    snprintf(p->name + n, sizeof p->name - n, "_m1");
 }
 
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out);
@@ -251,7 +269,7 @@ struct TileCost {
   const char* name;
   double step_us, tile_us;
 };
-constexpr TileCost kTileCosts[] = {
+constexpr TileCost kTileCosts[] = {  // in this order (the mixed plan takes [1])
     {kBig, 1.4295, 2.6456}, {kMid, 0.8187, 1.9745}, {kMid128, 0.4817, 1.8138}};
 constexpr double kPartialPass = 0.6767;
 constexpr double kLaunchUs = 1.1184;
@@ -294,19 +312,24 @@ double launch_cost(const TileCost& c, int64_t tiles, int64_t S, int64_t k_tiles,
 // K split 2, 3, 4, 6 or 8 ways (at least 8 K-steps a slice, at most 4
 // workgroups per CU, partials within the no-allocation scratch), and the
 // hybrids of an unsplit plan whose last pass is partial, its left-over
-// columns split 2, 3, 4, 6 or 8 ways.
+// columns split 2, 3, 4, 6 or 8 ways, and for the 256 x 256 tile the mixed
+// plan, its left-over columns unsplit on 256 x 128 tiles.
 Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
   Plan best{};
   double best_t = 0;
-  auto consider = [&](const TileConfig* t, int64_t S, int64_t h, double cost) {
+  auto consider = [&](const TileConfig* t, int64_t S, int64_t h, double cost,
+                      const TileConfig* tail = nullptr) {
     if (best.tile && cost >= best_t) return;
     best = Plan{};
     best.tile = t;
     best.splits = (int)S;
     best.tail_splits = (int)h;
+    best.tail_tile = tail;
     best.group_m = 4;
     best_t = cost;
   };
+  const TileConfig* big = find_tile_config(kBig);
+  const TileConfig* mid = find_tile_config(kMid);
   for (const TileCost& c : kTileCosts) {
     const TileConfig* t = find_tile_config(c.name);
     if (!t || (half && !t->f16)) continue;
@@ -331,6 +354,16 @@ Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
         const double est = launch_cost(c, tm * head_cols, 1, kt, M, n1) +
                            launch_cost(c, tm * (tn - head_cols), hs, kt, M, N - n1);
         consider(t, 1, hs, tm * head_cols / kCUs >= 2 ? est * (1 + kHybridMargin) : est);
+      }
+      // mixed: the same head, the columns after it unsplit on 256 x 128
+      // tiles (the same margin as a hybrid after two or more whole passes)
+      if (t == big && mid && (!half || mid->f16)) {
+        const TileCost& mc = kTileCosts[1];
+        const int64_t mkt = (K + mid->bk - 1) / mid->bk;
+        const int64_t mtiles = ((M + mid->bm - 1) / mid->bm) * ((N - n1 + mid->bn - 1) / mid->bn);
+        const double est = launch_cost(c, tm * head_cols, 1, kt, M, n1) +
+                           launch_cost(mc, mtiles, 1, mkt, M, N - n1);
+        consider(t, 1, 0, tm * head_cols / kCUs >= 2 ? est * (1 + kHybridMargin) : est, mid);
       }
     }
   }
@@ -435,16 +468,18 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
   return p;
 }
 
-// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>][_n<0|1>][_h<splits>]"
+// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>][_n<0|1>][_h<splits>][_m<0|1>]"
 // where tile is a table name (_P: a persistent grid of that many workgroups
 // walking the tiles; only for tiles built with it, bf16 operands, and never
 // split.  _n1: non-temporal B loads, only for tiles built with them.  _h:
-// the hybrid of finish_plan, only with _k1 and no _P).
+// the hybrid of finish_plan, only with _k1 and no _P.  _m1: the mixed plan
+// of finish_plan, only on the 256 x 256 tile with _k1 and none of _P, _n1
+// and _h).
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out) {
   char buf[64];
   if (strlen(name) >= sizeof buf) return false;
   strcpy(buf, name);
-  int splits = 1, group = 4, rot = 0, persist = 0, stream = 0, tail = 0;
+  int splits = 1, group = 4, rot = 0, persist = 0, stream = 0, tail = 0, mixed = 0;
   for (;;) {
     char* u = strrchr(buf, '_');
     if (!u) break;
@@ -467,6 +502,9 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
     } else if (u[1] == 'h' && sscanf(u + 2, "%d", &v) == 1 && v >= 0) {
       tail = v;
       *u = 0;
+    } else if (u[1] == 'm' && sscanf(u + 2, "%d", &v) == 1 && (v == 0 || v == 1)) {
+      mixed = v;
+      *u = 0;
     } else {
       break;
     }
@@ -476,6 +514,8 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
   if (persist > 0 && (!t->persist || splits > 1)) return false;
   if (stream && !t->stream) return false;
   if (tail > 1 && (splits > 1 || persist > 0)) return false;
+  if (mixed && (t != find_tile_config(kBig) || splits > 1 || persist > 0 || stream || tail > 1))
+    return false;
   out->tile = t;
   out->splits = splits;
   out->group_m = group;
@@ -483,6 +523,7 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
   out->persist = persist;
   out->stream_b = stream;
   out->tail_splits = tail;
+  out->tail_tile = mixed ? find_tile_config(kMid) : nullptr;
   finish_plan(out, M, N, K);
   return true;
 }
@@ -585,9 +626,11 @@ int run_one(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64
 // A plan on C: a hybrid plan as two calls on column ranges, each a plain
 // plan of the same tile -- columns [split_n, N) with K split tail_splits
 // ways first (it is the part that may need a workspace, so an error there
-// leaves nothing enqueued), then columns [0, split_n) unsplit.  The two
+// leaves nothing enqueued), then columns [0, split_n) unsplit.  A mixed plan
+// the same way, with the columns [split_n, N) unsplit on tail_tile.  The two
 // ranges share no element of C, so each element's sum is that of the plan
-// that covers it.
+// that covers it (for a mixed plan without rotation the same as the plain
+// plan's: both tiles add the same K-steps in the same order).
 int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
         const void* B, int64_t ldb, void* C, int64_t ldc, bool out_f32, bool half,
         hipStream_t stream, void* fixed_ws = nullptr, size_t fixed_bytes = 0) {
@@ -598,12 +641,18 @@ int run(const Plan& p, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   Plan part = p;
   part.split_n = 0;
   part.tail_splits = 0;
+  part.tail_tile = nullptr;
   part.splits = p.tail_splits;
+  if (p.tail_tile) {
+    part.tile = p.tail_tile;
+    part.splits = 1;
+  }
   const uint16_t* B1 = (const uint16_t*)B + n1 * ldb;
   uint8_t* C1 = (uint8_t*)C + n1 * (out_f32 ? 4 : 2);
   int rc = run_one(part, M, N - n1, K, A, lda, B1, ldb, C1, ldc, out_f32, half, stream,
                    fixed_ws, fixed_bytes);
   if (rc != GEMM_OK) return rc;
+  part.tile = p.tile;
   part.splits = 1;
   return run_one(part, M, n1, K, A, lda, B, ldb, C, ldc, out_f32, half, stream, fixed_ws,
                  fixed_bytes);

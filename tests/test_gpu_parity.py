@@ -627,6 +627,64 @@ def test_hybrid_f16_bit_exact():
     assert rep["ok"], rep
 
 
+# ------------------------------------------------------------ mixed plans
+# "_m1": the tile columns that fill whole passes run on 256 x 256 tiles, the
+# columns after them unsplit on 256 x 128 tiles.  520 x 22920: 3 rows x 90
+# columns of 256 x 256 tiles, so the head is 85 columns (21760) and the tail
+# 1160 columns (3 x 10 tiles of 256 x 128, the last one ragged).
+MIXED = "t256x256x64_w2x2_s2_x3_p10_k1_g4_m1"
+
+
+def test_mixed_plan_bit_exact():
+    """Integer inputs, K = 456 (a partial last K-step): the mixed plan is
+    bit-exact in bf16 and fp32 output, over fp16 operands and through the
+    no-allocation entry point."""
+    import torch
+
+    import dense_gemm_bf16_amd as g
+
+    M, N, K = 520, 22920, 456
+    A = int_bf16(M, K, seed=1540)
+    B = int_bf16(N, K, seed=1541)
+    ref16, ref64 = _oracle().gemm(A, B)
+    rep = check_bf16(run_gemm(A, B, config=MIXED), ref16, None, K, exact=True)
+    print("bf16", rep, flush=True)
+    assert rep["ok"], rep
+    assert check_f32(run_gemm(A, B, config=MIXED, out_f32=True), ref64, K, exact=True)["ok"]
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    ldc = (N + 7) // 8 * 8
+    dC = torch.zeros((M, ldc), dtype=torch.int16, device="cuda")
+    g.gemm_bf16_ex_noalloc(MIXED, M, N, K, dA, K, dB, K, dC, ldc)
+    torch.cuda.synchronize()
+    assert np.array_equal(dC[:, :N].cpu().numpy().view(np.uint16), ref16)
+    A16 = int_bf16(M, K, seed=1542, lo=-16, hi=16, fmt="f16")
+    B16 = int_bf16(N, K, seed=1543, lo=-16, hi=16, fmt="f16")
+    r16, _ = _oracle().gemm(A16, B16, fmt="f16")
+    rep = check_bf16(run_gemm(A16, B16, config=MIXED, fmt="f16"), r16, None, K, exact=True,
+                     fmt="f16")
+    print("f16", rep, flush=True)
+    assert rep["ok"], rep
+
+
+def test_mixed_plan_is_the_plain_plans_bits():
+    """N(0,1) inputs: the mixed plan gives the plain 256 x 256 plan's bits in
+    every column (both tiles add the same K-steps in the same order), in
+    bf16 and fp32 output, and meets the ulp criterion against the oracle."""
+    M, N, K = 520, 22920, 1000
+    A = normal_bf16(M, K, seed=1550)
+    B = normal_bf16(N, K, seed=1551)
+    plain = "t256x256x64_w2x2_s2_x3_p10_k1_g4"
+    got = run_gemm(A, B, config=MIXED)
+    assert np.array_equal(got, run_gemm(A, B, config=plain))
+    got32 = run_gemm(A, B, config=MIXED, out_f32=True)
+    assert np.array_equal(got32, run_gemm(A, B, config=plain, out_f32=True))
+    ref16, ref64 = _oracle().gemm(A, B)
+    rep = check_bf16(got, ref16, ref64, K)
+    print(rep, flush=True)
+    assert rep["ok"], rep
+
+
 def test_automatic_hybrid_plan_on_a_qkv_shape():
     """2048 x 10240 x 8192 (a 70B-class fused QKV projection at 2048 tokens):
     320 tiles of 256 x 256, and the automatic plan is hybrid; full rows and
