@@ -216,14 +216,16 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
   }
   if (p->split_n == 0) p->tail_splits = 0;
   // Mixed: the same head as the hybrid, the columns after it unsplit on
-  // tail_tile (only 256 x 256 over 256 x 128, unsplit, no persistent grid,
-  // no non-temporal B); otherwise the plain plan.
+  // tail_tile (only 256 x 256 over 256 x 128 or 128 x 128, unsplit, no
+  // persistent grid, no non-temporal B); otherwise the plain plan.
+  int mixed = 0;
   if (p->tail_tile) {
     const int64_t tiles_m = (M + p->tile->bm - 1) / p->tile->bm;
     const int64_t tiles_n = (N + p->tile->bn - 1) / p->tile->bn;
     const int64_t head_cols = tiles_m > 0 ? (tiles_m * tiles_n / kCUs) * kCUs / tiles_m : 0;
+    mixed = p->tail_tile == find_tile_config(kMid) ? 1 : p->tail_tile == find_tile_config(kMid128) ? 2 : 0;
     const bool ok = p->split_n == 0 && p->splits == 1 && p->persist == 0 && p->stream_b == 0 &&
-                    p->tile == find_tile_config(kBig) && p->tail_tile == find_tile_config(kMid);
+                    p->tile == find_tile_config(kBig) && mixed > 0;
     if (ok && head_cols > 0 && head_cols < tiles_n)
       p->split_n = head_cols * p->tile->bn;
     else
@@ -239,7 +241,7 @@ void finish_plan(Plan* p, int64_t M, int64_t N, int64_t K) {
   if (p->split_n > 0 && !p->tail_tile && n > 0 && n < (int)sizeof p->name)
     snprintf(p->name + n, sizeof p->name - n, "_h%d", p->tail_splits);
   if (p->tail_tile && n > 0 && n < (int)sizeof p->name)
-    snprintf(p->name + n, sizeof p->name - n, "_m1");
+    snprintf(p->name + n, sizeof p->name - n, "_m%d", mixed);
 }
 
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out);
@@ -269,7 +271,7 @@ struct TileCost {
   const char* name;
   double step_us, tile_us;
 };
-constexpr TileCost kTileCosts[] = {  // in this order (the mixed plan takes [1])
+constexpr TileCost kTileCosts[] = {  // in this order (the mixed plans take [1] and [2])
     {kBig, 1.4295, 2.6456}, {kMid, 0.8187, 1.9745}, {kMid128, 0.4817, 1.8138}};
 constexpr double kPartialPass = 0.6767;
 constexpr double kLaunchUs = 1.1184;
@@ -313,7 +315,7 @@ double launch_cost(const TileCost& c, int64_t tiles, int64_t S, int64_t k_tiles,
 // workgroups per CU, partials within the no-allocation scratch), and the
 // hybrids of an unsplit plan whose last pass is partial, its left-over
 // columns split 2, 3, 4, 6 or 8 ways, and for the 256 x 256 tile the mixed
-// plan, its left-over columns unsplit on 256 x 128 tiles.
+// plans, its left-over columns unsplit on 256 x 128 or 128 x 128 tiles.
 Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
   Plan best{};
   double best_t = 0;
@@ -330,6 +332,7 @@ Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
   };
   const TileConfig* big = find_tile_config(kBig);
   const TileConfig* mid = find_tile_config(kMid);
+  const TileConfig* m128 = find_tile_config(kMid128);
   for (const TileCost& c : kTileCosts) {
     const TileConfig* t = find_tile_config(c.name);
     if (!t || (half && !t->f16)) continue;
@@ -356,14 +359,17 @@ Plan model_plan(int64_t M, int64_t N, int64_t K, bool half) {
         consider(t, 1, hs, tm * head_cols / kCUs >= 2 ? est * (1 + kHybridMargin) : est);
       }
       // mixed: the same head, the columns after it unsplit on 256 x 128
-      // tiles (the same margin as a hybrid after two or more whole passes)
-      if (t == big && mid && (!half || mid->f16)) {
-        const TileCost& mc = kTileCosts[1];
-        const int64_t mkt = (K + mid->bk - 1) / mid->bk;
-        const int64_t mtiles = ((M + mid->bm - 1) / mid->bm) * ((N - n1 + mid->bn - 1) / mid->bn);
+      // or 128 x 128 tiles (the same margin as a hybrid after two or more
+      // whole passes)
+      for (int i = 1; i <= 2 && t == big; ++i) {
+        const TileConfig* tt = i == 1 ? mid : m128;
+        if (!tt || (half && !tt->f16)) continue;
+        const TileCost& mc = kTileCosts[i];
+        const int64_t mkt = (K + tt->bk - 1) / tt->bk;
+        const int64_t mtiles = ((M + tt->bm - 1) / tt->bm) * ((N - n1 + tt->bn - 1) / tt->bn);
         const double est = launch_cost(c, tm * head_cols, 1, kt, M, n1) +
                            launch_cost(mc, mtiles, 1, mkt, M, N - n1);
-        consider(t, 1, 0, tm * head_cols / kCUs >= 2 ? est * (1 + kHybridMargin) : est, mid);
+        consider(t, 1, 0, tm * head_cols / kCUs >= 2 ? est * (1 + kHybridMargin) : est, tt);
       }
     }
   }
@@ -468,13 +474,13 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, bool half = false) {
   return p;
 }
 
-// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>][_n<0|1>][_h<splits>][_m<0|1>]"
+// Parse "tile[_k<splits>][_g<group>][_r<rotation>][_P<grid>][_n<0|1>][_h<splits>][_m<0|1|2>]"
 // where tile is a table name (_P: a persistent grid of that many workgroups
 // walking the tiles; only for tiles built with it, bf16 operands, and never
 // split.  _n1: non-temporal B loads, only for tiles built with them.  _h:
-// the hybrid of finish_plan, only with _k1 and no _P.  _m1: the mixed plan
-// of finish_plan, only on the 256 x 256 tile with _k1 and none of _P, _n1
-// and _h).
+// the hybrid of finish_plan, only with _k1 and no _P.  _m1 / _m2: the mixed
+// plan of finish_plan with its tail on 256 x 128 / 128 x 128 tiles, only on
+// the 256 x 256 tile with _k1 and none of _P, _n1 and _h).
 bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out) {
   char buf[64];
   if (strlen(name) >= sizeof buf) return false;
@@ -502,7 +508,7 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
     } else if (u[1] == 'h' && sscanf(u + 2, "%d", &v) == 1 && v >= 0) {
       tail = v;
       *u = 0;
-    } else if (u[1] == 'm' && sscanf(u + 2, "%d", &v) == 1 && (v == 0 || v == 1)) {
+    } else if (u[1] == 'm' && sscanf(u + 2, "%d", &v) == 1 && v >= 0 && v <= 2) {
       mixed = v;
       *u = 0;
     } else {
@@ -523,7 +529,7 @@ bool plan_from_name(const char* name, int64_t M, int64_t N, int64_t K, Plan* out
   out->persist = persist;
   out->stream_b = stream;
   out->tail_splits = tail;
-  out->tail_tile = mixed ? find_tile_config(kMid) : nullptr;
+  out->tail_tile = mixed == 1 ? find_tile_config(kMid) : mixed == 2 ? find_tile_config(kMid128) : nullptr;
   finish_plan(out, M, N, K);
   return true;
 }

@@ -44,8 +44,9 @@ struct Plan {
   int tail_splits;
   int64_t split_n;
   // Mixed: as the hybrid, but the columns from split_n on run unsplit on
-  // this narrower tile (the 256 x 128 one under 256 x 256), which fills the
-  // CUs where the wide tile's last pass would be half empty (null: not mixed).
+  // this narrower tile (256 x 128 or 128 x 128 under 256 x 256), which fills
+  // the CUs where the wide tile's last pass would be part empty (null: not
+  // mixed).
   const TileConfig* tail_tile;
   char name[64];
 };

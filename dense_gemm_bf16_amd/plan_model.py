@@ -18,8 +18,9 @@ one; every launch adds ``launch_us``; a split adds ``split_us`` plus
 bytes).  A hybrid plan is two launches: the whole passes' tile columns
 unsplit, and the remaining columns with K split; with two or more whole
 passes it must beat the other plans by HYBRID_MARGIN.  A mixed plan
-(``_m1``, 256 x 256 tiles only) is the same two launches with the remaining
-columns unsplit on 256 x 128 tiles, under the same margin.
+(``_m1`` / ``_m2``, 256 x 256 tiles only) is the same two launches with the
+remaining columns unsplit on 256 x 128 / 128 x 128 tiles, under the same
+margin.
 
 Usage::
 
@@ -55,8 +56,9 @@ TILES = {
     "t128x128x64_w2x2_s4_x3_p10": (128, 128, 2),
 }
 BK = 64
-PLAN = re.compile(r"^(t\d+x\d+x64_w2x2_s\d_x3_p10)_k(\d+)_g\d+(_r\d+)?(_h(\d+))?(_n1)?(_m1)?$")
-BIG, MID = "t256x256x64_w2x2_s2_x3_p10", "t256x128x64_w2x2_s3_x3_p10"
+PLAN = re.compile(r"^(t\d+x\d+x64_w2x2_s\d_x3_p10)_k(\d+)_g\d+(_r\d+)?(_h(\d+))?(_n1)?(_m[12])?$")
+BIG, MID, M128 = ("t256x256x64_w2x2_s2_x3_p10", "t256x128x64_w2x2_s3_x3_p10",
+                  "t128x128x64_w2x2_s4_x3_p10")
 # constant order: step_us[3], tile_us[3], partial, split_us, split_us_per_mb, launch_us
 NAMES = ["step_us_256x256", "step_us_256x128", "step_us_128x128", "tile_us_256x256",
          "tile_us_256x128", "tile_us_128x128", "partial", "split_us", "split_us_per_mb",
@@ -86,11 +88,11 @@ def launches(plan: str, M: int, N: int, K: int):
     h = int(m.group(5) or 0)
     if m.group(7) and S == 1 and not h and m.group(1) == BIG:
         # mixed: the whole passes' columns on 256 x 256 tiles, the rest
-        # unsplit on 256 x 128 tiles
+        # unsplit on 256 x 128 (_m1) or 128 x 128 (_m2) tiles
         head_cols = (tm * tn // CUS) * CUS // tm
         if 0 < head_cols < tn:
             n1 = head_cols * bn
-            mbm, mbn, mti = TILES[MID]
+            mbm, mbn, mti = TILES[MID if m.group(7) == "_m1" else M128]
             return [(ti, tm * head_cols, 1, kt, M, n1),
                     (mti, -(-M // mbm) * -(-(N - n1) // mbn), 1, kt, M, N - n1)]
     if h and S == 1:
@@ -160,7 +162,7 @@ def candidates(M: int, N: int, K: int) -> list[str]:
                     continue
                 out.append(f"{name}_k1_g4_h{hs}")
             if name == BIG:
-                out.append(f"{name}_k1_g4_m1")
+                out += [f"{name}_k1_g4_m1", f"{name}_k1_g4_m2"]
     return list(dict.fromkeys(out))
 
 

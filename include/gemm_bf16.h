@@ -124,7 +124,7 @@ int gemm_bf16_ex(const char* config,
  * "t256x256x64_w2x2_s2_x3_p10_k1_g4": tile BM x BN x BK, waves, ring stages,
  * LDS swizzle, load schedule, then K splits and GROUP_M (and "_r<n>", the
  * K-step rotation, when on, "_n1" when B is loaded non-temporally,
- * "_h<S>" for a hybrid plan and "_m1" for a mixed one).
+ * "_h<S>" for a hybrid plan and "_m1" / "_m2" for a mixed one).
  * Per-thread static storage, valid until the thread's next call; never NULL.
  *
  * "_h<S>" (a hybrid plan; with "_k1" only, and not with "_P"): where the
@@ -140,11 +140,12 @@ int gemm_bf16_ex(const char* config,
  * tiles times S fit in one pass.  Named on a shape where it does not apply (whole passes, one pass or
  * less, or too few K-steps to split), it is dropped and the plain plan runs.
  *
- * "_m1" (a mixed plan; on the 256 x 256 tile t256x256x64_w2x2_s2_x3_p10
- * only, with "_k1", and not with "_P" or "_h"): the same whole passes as a
- * hybrid, columns 0 .. N1-1 on 256 x 256 tiles, and columns N1 .. N-1 as a
- * second launch on 256 x 128 tiles, unsplit, so the narrower tiles fill the
- * compute units that the wide tiles' last pass would leave idle.  No
+ * "_m1" / "_m2" (a mixed plan; on the 256 x 256 tile
+ * t256x256x64_w2x2_s2_x3_p10 only, with "_k1", and not with "_P" or "_h"):
+ * the same whole passes as a hybrid, columns 0 .. N1-1 on 256 x 256 tiles,
+ * and columns N1 .. N-1 as a second launch on 256 x 128 ("_m1") or
+ * 128 x 128 ("_m2") tiles, unsplit, so the narrower tiles fill the compute
+ * units that the wide tiles' last pass would leave idle.  No
  * workspace.  Both tiles add the same K-steps in the same order, so the
  * result is the plain plan's, bit for bit (with "_r<n>" the rotation
  * follows each launch's own tiles).  The automatic choice weighs it against

@@ -158,7 +158,7 @@ def test_hybrid_plan_names_on_the_host(lib):
     so = lib._lib
     fake = ctypes.c_void_p(0x10000)
     big = "t256x256x64_w2x2_s2_x3_p10"
-    assert "_h" in lib.config_name(2048, 10240, 8192)
+    assert "_h" in lib.config_name(1024, 10240, 8192)
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 28672, 8192),
                     (1024, 28672, 8192), (256, 8192, 8192), (300, 520, 456)]:
         assert "_h" not in lib.config_name(M, N, K), (M, N, K)
@@ -193,13 +193,14 @@ def test_hybrid_plan_names_on_the_host(lib):
 
 
 def test_mixed_plan_names_on_the_host(lib):
-    """Mixed plans (_m1): the whole passes of 256 x 256 tiles as whole tile
-    columns, the columns after them unsplit on 256 x 128 tiles, which fill
-    the CUs that the wide tiles' half-full last pass would leave idle.
-    Chosen automatically on such shapes (3.5 and 2.5 passes below) and on
-    none of the metric shapes or a 1.75-pass shape; no workspace.  Named,
-    accepted on the 256 x 256 tile with _k1 (M = 0, so nothing is launched)
-    and refused with a split, on another tile, or with _h or _P."""
+    """Mixed plans (_m1 / _m2): the whole passes of 256 x 256 tiles as whole
+    tile columns, the columns after them unsplit on 256 x 128 / 128 x 128
+    tiles, which fill the CUs that the wide tiles' part-full last pass would
+    leave idle.  Chosen automatically on such shapes (_m1 at 3.5 and 2.5
+    passes, _m2 at 1.25 below) and on none of the metric shapes or a
+    1.75-pass shape; no workspace.  Named, accepted on the 256 x 256 tile
+    with _k1 (M = 0, so nothing is launched) and refused with a split, on
+    another tile, with _h or _P, or with another tail."""
     so = lib._lib
     fake = ctypes.c_void_p(0x10000)
     big = "t256x256x64_w2x2_s2_x3_p10"
@@ -207,15 +208,20 @@ def test_mixed_plan_names_on_the_host(lib):
     for M, N, K in [(2048, 28672, 4096), (4096, 14336, 8192), (2048, 20480, 4096)]:
         assert lib.config_name(M, N, K) == big + "_k1_g4_m1", (M, N, K)
         assert lib.workspace_size(M, N, K) == 0
+    for M, N, K in [(2048, 10240, 4096), (2048, 10240, 8192), (1024, 20480, 4096)]:
+        assert lib.config_name(M, N, K) == big + "_k1_g4_m2", (M, N, K)
+        assert lib.workspace_size(M, N, K) == 0
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 28672, 8192),
-                    (1024, 28672, 4096), (2048, 10240, 8192), (256, 8192, 8192)]:
-        assert "_m1" not in lib.config_name(M, N, K), (M, N, K)
+                    (1024, 28672, 4096), (1024, 10240, 8192), (256, 8192, 8192)]:
+        assert "_m" not in lib.config_name(M, N, K), (M, N, K)
 
     def rc(name):
         return so.gemm_bf16_ex(name.encode(), 0, 8, 8, None, 8, None, 8, fake, 8, 0, None)
 
     assert rc(big + "_k1_g4_m1") == lib.GEMM_OK
+    assert rc(big + "_k1_g4_m2") == lib.GEMM_OK
     assert rc(big + "_k1_g4_m0") == lib.GEMM_OK
+    assert rc(big + "_k1_g4_m3") == lib.GEMM_ERR_UNSUPPORTED
     assert rc(big + "_k2_g4_m1") == lib.GEMM_ERR_UNSUPPORTED
     assert rc(mid + "_k1_g4_m1") == lib.GEMM_ERR_UNSUPPORTED
     assert rc(big + "_k1_g4_h2_m1") == lib.GEMM_ERR_UNSUPPORTED
@@ -235,7 +241,7 @@ def test_model_plans_keep_the_metric_shapes_and_fill_the_chip(lib):
     assert lib.config_name(512, 8192, 5376) == "t128x128x64_w2x2_s4_x3_p10_k1_g4"
     assert lib.config_name(3072, 4096, 4096) == big + "_k1_g4"
     assert lib.config_name(768, 4096, 14336) == big + "_k4_g4"
-    plan = re.compile(r"^t(\d+)x(\d+)x(\d+)_w\dx\d_s\d+_x\d_p\d+_k(\d+)_g\d+(_h\d+|_m1)?$")
+    plan = re.compile(r"^t(\d+)x(\d+)x(\d+)_w\dx\d_s\d+_x\d_p\d+_k(\d+)_g\d+(_h\d+|_m[12])?$")
     for M in (257, 300, 384, 640, 1000, 2500, 5000):
         for N in (512, 3000, 4096, 11008, 14336):
             for K in (256, 1000, 4096, 14336):

@@ -628,14 +628,16 @@ def test_hybrid_f16_bit_exact():
 
 
 # ------------------------------------------------------------ mixed plans
-# "_m1": the tile columns that fill whole passes run on 256 x 256 tiles, the
-# columns after them unsplit on 256 x 128 tiles.  520 x 22920: 3 rows x 90
-# columns of 256 x 256 tiles, so the head is 85 columns (21760) and the tail
-# 1160 columns (3 x 10 tiles of 256 x 128, the last one ragged).
-MIXED = "t256x256x64_w2x2_s2_x3_p10_k1_g4_m1"
+# "_m1" / "_m2": the tile columns that fill whole passes run on 256 x 256
+# tiles, the columns after them unsplit on 256 x 128 / 128 x 128 tiles.
+# 520 x 22920: 3 rows x 90 columns of 256 x 256 tiles, so the head is 85
+# columns (21760) and the tail 1160 columns (3 x 10 tiles of 256 x 128, or
+# 5 x 10 of 128 x 128; the last column ragged).
+MIXED_PLANS = ["t256x256x64_w2x2_s2_x3_p10_k1_g4_m1", "t256x256x64_w2x2_s2_x3_p10_k1_g4_m2"]
 
 
-def test_mixed_plan_bit_exact():
+@pytest.mark.parametrize("MIXED", MIXED_PLANS)
+def test_mixed_plan_bit_exact(MIXED):
     """Integer inputs, K = 456 (a partial last K-step): the mixed plan is
     bit-exact in bf16 and fp32 output, over fp16 operands and through the
     no-allocation entry point."""
@@ -667,7 +669,8 @@ def test_mixed_plan_bit_exact():
     assert rep["ok"], rep
 
 
-def test_mixed_plan_is_the_plain_plans_bits():
+@pytest.mark.parametrize("MIXED", MIXED_PLANS)
+def test_mixed_plan_is_the_plain_plans_bits(MIXED):
     """N(0,1) inputs: the mixed plan gives the plain 256 x 256 plan's bits in
     every column (both tiles add the same K-steps in the same order), in
     bf16 and fp32 output, and meets the ulp criterion against the oracle."""
@@ -685,22 +688,23 @@ def test_mixed_plan_is_the_plain_plans_bits():
     assert rep["ok"], rep
 
 
-def test_automatic_hybrid_plan_on_a_qkv_shape():
-    """2048 x 10240 x 8192 (a 70B-class fused QKV projection at 2048 tokens):
-    320 tiles of 256 x 256, and the automatic plan is hybrid; full rows and
-    columns on both sides of the split column are checked against the
-    oracle."""
+@pytest.mark.parametrize("M,N,K,kind", [(1024, 10240, 8192, "_h"), (2048, 10240, 8192, "_m2")])
+def test_automatic_split_plans_on_a_qkv_shape(M, N, K, kind):
+    """A 70B-class fused QKV projection (N = 10240, K = 8192) at 1024 and
+    2048 tokens: the tiles make 1.25 passes over the CUs, and the automatic
+    plan is a hybrid (256 x 128 tiles, the tail split along K) or a mixed one
+    (256 x 256 tiles, the tail on 128 x 128 tiles); full rows and columns on
+    both sides of the split column are checked against the oracle."""
     import dense_gemm_bf16_amd as g
 
-    M, N, K = 2048, 10240, 8192
     plan = g.config_name(M, N, K)
     print("plan", plan, flush=True)
-    assert "_h" in plan, plan
+    assert kind in plan, plan
     A = normal_bf16(M, K, seed=1530)
     B = normal_bf16(N, K, seed=1531, std=K ** -0.5)
     got = run_gemm(A, B)
     o = _oracle()
-    rows = np.array([0, 1, 255, 256, 1000, 2047])
+    rows = np.array([0, 1, 255, 256, M // 2 + 3, M - 1])
     cols = np.array([0, 8191, 8192, 8193, 9000, 10239])
     r16, r64 = o.gemm(np.ascontiguousarray(A[rows]), B)
     rep = check_bf16(got[rows], r16, r64, K, 1.0, K ** -0.5)
