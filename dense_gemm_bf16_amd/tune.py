@@ -4,7 +4,7 @@ the library's plan choice consults first (``csrc/gemm_tuned.inc``).
 
 A plan is a configuration name of the library (``gemm_bf16_config_at``)
 plus the K split count, raster grouping and K-step rotation
-(``<tile>_k<S>_g<G>[_r<R>][_n1][_h<S>]``), exactly the names ``gemm_bf16_ex``
+(``<tile>_k<S>_g<G>[_r<R>][_n1][_h<S>|_m<1|2>]``), exactly the names ``gemm_bf16_ex``
 accepts.
 For each shape the sweep
 
@@ -13,7 +13,8 @@ For each shape the sweep
    K-steps per slice and at most ~4 workgroups per CU; GROUP_M 4 and 8;
    rotation off and on; with one row of tiles, non-temporal B loads off and
    on where the tile is built with them; with more than one pass of tiles
-   over the CUs and the last one partial, the hybrid plans "_h2" .. "_h4"),
+   over the CUs and the last one partial, the hybrid plans "_h2" .. "_h4"
+   and, on the 256 x 256 tile, the mixed plans "_m1" and "_m2"),
 2. times every candidate briefly (HIP events on one stream, after a warm-up
    long enough for the clock to settle; memory-bound shapes cycle through
    copies of B larger than the 256 MB Infinity Cache, as ``bench.py`` does),
@@ -88,7 +89,14 @@ def candidates(M: int, N: int, K: int, tiles: list[str], cus: int = 256,
                         out.append(name + "_n1")
                     if hybrid:
                         out += [f"{name}_h{h}" for h in (2, 3, 4) if k_tiles // h >= 4]
+                        if tile == MIXED_TILE:
+                            out += [f"{name}_m1", f"{name}_m2"]
     return out
+
+
+# the tile whose plans take a mixed tail ("_m1": 256 x 128 tiles, "_m2":
+# 128 x 128 tiles for the columns past the whole passes)
+MIXED_TILE = "t256x256x64_w2x2_s2_x3_p10"
 
 
 def stream_tiles(g, tiles: list[str]) -> frozenset:

@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TABLE = os.path.join(ROOT, "dense_gemm_bf16_amd", "csrc", "gemm_tuned.inc")
-PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d+)_k(\d+)_g(\d+)(_r\d+)?(_n1)?(_h\d+)?$")
+PLAN = re.compile(r"^(t\d+x\d+x\d+_w\dx\d_s\d+_x\d_p\d+)_k(\d+)_g(\d+)(_r\d+)?(_n1)?(_h\d+|_m[12])?$")
 ROW = re.compile(r'^\{(\d+), (\d+), (\d+), "([^"]+)"\},$')
 
 
@@ -90,6 +90,33 @@ def test_hybrid_candidates_only_past_one_partial_pass(lib):
             assert rc == lib.GEMM_OK, p
     assert any("_h" in p for p in candidates(2048, 10240, 8192, tiles))
     assert not any("_h" in p for p in candidates(4096, 4096, 4096, tiles))
+
+
+def test_mixed_candidates_on_the_wide_tile_past_one_partial_pass(lib):
+    """_m1 / _m2 candidates exist only on the 256 x 256 tile, for unsplit
+    plans whose tiles make more than one pass with the last one partial, and
+    every one is a name the library accepts (M = 0: nothing is launched)."""
+    import ctypes
+
+    from dense_gemm_bf16_amd.tune import MIXED_TILE, candidates, parse_tile
+
+    tiles = lib.config_names()
+    fake = ctypes.c_void_p(0x10000)
+    for M, N, K in [(2048, 10240, 8192), (2048, 28672, 4096), (4096, 4096, 4096),
+                    (256, 8192, 8192)]:
+        for p in candidates(M, N, K, tiles):
+            if "_m" not in p:
+                continue
+            m = PLAN.match(p)
+            assert m and m.group(1) == MIXED_TILE and m.group(2) == "1", p
+            bm, bn, _ = parse_tile(m.group(1))
+            n_tiles = -(-M // bm) * -(-N // bn)
+            assert n_tiles > 256 and n_tiles % 256, p
+            rc = lib._lib.gemm_bf16_ex(p.encode(), 0, 64, 64, fake, 64, fake, 64, fake, 64, 0,
+                                       None)
+            assert rc == lib.GEMM_OK, p
+    assert any(p.endswith("_m2") for p in candidates(2048, 10240, 8192, tiles))
+    assert not any("_m" in p for p in candidates(4096, 4096, 4096, tiles))
 
 
 def test_written_table_format(tmp_path):
