@@ -2,8 +2,8 @@
 
 ``choose_plan`` (``csrc/gemm_api.hip``, ``model_plan``) picks, for M > 256,
 the plan with the lowest estimated time among the three direct-to-LDS tiles
-(256 x 256, 256 x 128, 128 x 128), K split 1, 2, 3, 4, 6 or 8 ways and the
-hybrid plans.  This module holds the same model in Python, the sweep that
+(256 x 256, 256 x 128, 128 x 128), K split 1, 2, 3, 4, 6 or 8 ways, the
+hybrid plans and the mixed plans.  This module holds the same model in Python, the sweep that
 measures plans on the GPU, and the fit of the model's ten constants to
 those measurements, so the constants compiled into the library can be
 re-derived and checked.
