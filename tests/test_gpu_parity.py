@@ -688,6 +688,38 @@ def test_mixed_plan_is_the_plain_plans_bits(MIXED):
     assert rep["ok"], rep
 
 
+def test_random_mixed_plans_bit_exact():
+    """Six seeded random mixed plans on shapes with a tail: 3 rows of 256 x
+    256 tiles over 90 columns, M, N and K ragged, the tail on 256 x 128 or
+    128 x 128 tiles, rotation and GROUP_M random, row strides padded with
+    NaN, fp32 output for one call in three; integer inputs, bit-exact."""
+    rng = np.random.default_rng(6161)
+    o = _oracle()
+    for i in range(6):
+        M = 512 + int(rng.integers(1, 256))
+        N = 89 * 256 + int(rng.integers(1, 256))
+        K = int(rng.integers(130, 500))
+        name = f"t256x256x64_w2x2_s2_x3_p10_k1_g{int(rng.choice([4, 8]))}"
+        if rng.random() < 0.5:
+            name += "_r1"
+        name += f"_m{1 + i % 2}"
+        pad_a, pad_b = 8 * int(rng.integers(0, 3)), 8 * int(rng.integers(0, 3))
+        kk = (K + 7) // 8 * 8
+        A = np.full((M, kk + pad_a), 0x7FC0, np.uint16)
+        B = np.full((N, kk + pad_b), 0x7FC0, np.uint16)
+        A[:, :K] = int_bf16(M, K, seed=1700 + 2 * i)
+        B[:, :K] = int_bf16(N, K, seed=1701 + 2 * i)
+        ref16, ref64 = o.gemm(A, B, K=K)
+        f32 = i % 3 == 0
+        got = run_gemm(A, B, K=K, config=name, out_f32=f32)
+        if f32:
+            rep = check_f32(got, ref64, K, exact=True)
+        else:
+            rep = check_bf16(got, ref16, None, K, exact=True)
+        print(i, name, (M, N, K), "f32" if f32 else "bf16", rep, flush=True)
+        assert rep["ok"], (name, (M, N, K), rep)
+
+
 @pytest.mark.parametrize("M,N,K,kind", [(1024, 10240, 8192, "_h"), (2048, 10240, 8192, "_m2")])
 def test_automatic_split_plans_on_a_qkv_shape(M, N, K, kind):
     """A 70B-class fused QKV projection (N = 10240, K = 8192) at 1024 and
