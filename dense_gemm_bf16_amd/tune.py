@@ -252,7 +252,7 @@ def main(argv=None) -> int:
             saved = json.load(f)
         entries = choose_entries(saved["results"], old, args.min_gain)
         note = (f"{len(entries)} of {len(saved['results'])} swept shapes in the table, rebuilt "
-                f"from {os.path.basename(args.from_json)} (min gain {args.min_gain:.0%})")
+                f"from {os.path.basename(args.from_json)} (min gain {args.min_gain * 100:g}%)")
         write_table(entries, args.out, note)
         print(note)
         return 0
@@ -284,7 +284,7 @@ def main(argv=None) -> int:
         results[f"{M}x{N}x{K}"] = tune_shape(M, N, K)
     entries = choose_entries(results, old, args.min_gain)
     note = (f"{len(entries)} of {len(shapes)} swept shapes in the table (min gain "
-            f"{args.min_gain:.0%}); sweep took {time.time() - t0:.0f} s")
+            f"{args.min_gain * 100:g}%); sweep took {time.time() - t0:.0f} s")
     write_table(entries, args.out, note)
     with open(args.json, "w") as f:
         json.dump({"note": note, "results": results}, f, indent=1)

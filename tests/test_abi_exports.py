@@ -256,9 +256,15 @@ def test_model_plans_keep_the_metric_shapes_and_fill_the_chip(lib):
 
 def test_rows_of_128_tiles_for_m_up_to_128(lib):
     """64 < M <= 128: one row of 128 x 128 tiles with K-step rotation and K
-    split to about 256 workgroups (the 256-row tiles would pad M to 256)."""
+    split to about 256 workgroups (the 256-row tiles would pad M to 256).
+    Shapes in the tuned table are the table's."""
+    from dense_gemm_bf16_amd.tune import read_table
+
+    tuned = set(read_table(os.path.join(ROOT, "dense_gemm_bf16_amd", "csrc", "gemm_tuned.inc")))
     for M in (65, 96, 128):
         for N, K in ((4096, 4096), (8192, 8192), (28672, 8192), (4096, 14336)):
+            if (M, N, K) in tuned:
+                continue
             name = lib.config_name(M, N, K)
             m = re.match(r"^t128x128x64_w2x2_s4_x3_p10_k(\d+)_g4_r1$", name)
             assert m, (M, N, K, name)
