@@ -205,15 +205,20 @@ def choose_entries(results: dict, old: dict, min_gain: float) -> list[tuple[int,
     is that table entry, not the static rules.  So: a shape gets the sweep's
     best plan if it beats the current choice by more than min_gain; else a
     shape already in the table keeps its entry (still within min_gain of the
-    best); else the automatic choice (cost model or rules) stays in charge."""
+    best); else the automatic choice (cost model or rules) stays in charge.
+    Rows of shapes this sweep did not time are kept as they are, after the
+    swept ones."""
     entries = []
+    swept = set()
     for key, r in results.items():
         M, N, K = (int(v) for v in key.split("x"))
+        swept.add((M, N, K))
         auto, auto_us = r["auto"]
         if r["best"] != auto and r["us"] < auto_us * (1 - min_gain):
             entries.append((M, N, K, r["best"]))
         elif (M, N, K) in old:
             entries.append((M, N, K, old[(M, N, K)]))
+    entries += [(M, N, K, plan) for (M, N, K), plan in old.items() if (M, N, K) not in swept]
     return entries
 
 
@@ -236,7 +241,7 @@ def write_table(entries: list[tuple[int, int, int, str]], path: str, note: str) 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workloads", default="all",
-                    help="comma-separated names from synthetic_inputs.WORKLOADS, or 'all'")
+                    help="comma-separated names from synthetic_inputs.WORKLOADS, 'all' or 'none'")
     ap.add_argument("--shapes", default="", help="extra shapes MxNxK,MxNxK")
     ap.add_argument("--out", default=os.path.join(_HERE, "csrc", "gemm_tuned.inc"))
     ap.add_argument("--json", default=os.path.join(_HERE, "csrc", "gemm_tuned.json"))
@@ -251,8 +256,9 @@ def main(argv=None) -> int:
         with open(args.from_json) as f:
             saved = json.load(f)
         entries = choose_entries(saved["results"], old, args.min_gain)
-        note = (f"{len(entries)} of {len(saved['results'])} swept shapes in the table, rebuilt "
-                f"from {os.path.basename(args.from_json)} (min gain {args.min_gain * 100:g}%)")
+        n_swept = sum(f"{M}x{N}x{K}" in saved["results"] for M, N, K, _ in entries)
+        note = (f"{len(entries)} rows, {n_swept} of them from the {len(saved['results'])} shapes of "
+                f"{os.path.basename(args.from_json)} (min gain {args.min_gain * 100:g}%)")
         write_table(entries, args.out, note)
         print(note)
         return 0
@@ -268,7 +274,7 @@ def main(argv=None) -> int:
         return 1
     torch.cuda.set_device(0)
     names = list(WORKLOADS) if args.workloads == "all" else [
-        w for w in args.workloads.split(",") if w]
+        w for w in args.workloads.split(",") if w and w != "none"]
     shapes = []
     for n in names:
         w = WORKLOADS[n]
@@ -283,7 +289,8 @@ def main(argv=None) -> int:
     for (M, N, K) in shapes:
         results[f"{M}x{N}x{K}"] = tune_shape(M, N, K)
     entries = choose_entries(results, old, args.min_gain)
-    note = (f"{len(entries)} of {len(shapes)} swept shapes in the table (min gain "
+    n_swept = sum(f"{M}x{N}x{K}" in results for M, N, K, _ in entries)
+    note = (f"{len(entries)} rows, {n_swept} of them from the {len(shapes)} swept shapes (min gain "
             f"{args.min_gain * 100:g}%); sweep took {time.time() - t0:.0f} s")
     write_table(entries, args.out, note)
     with open(args.json, "w") as f:

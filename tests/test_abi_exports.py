@@ -158,7 +158,7 @@ def test_hybrid_plan_names_on_the_host(lib):
     so = lib._lib
     fake = ctypes.c_void_p(0x10000)
     big = "t256x256x64_w2x2_s2_x3_p10"
-    assert "_h" in lib.config_name(1024, 10240, 8192)
+    assert "_h" in lib.config_name(2048, 5376, 8192)
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 28672, 8192),
                     (1024, 28672, 8192), (256, 8192, 8192), (300, 520, 456)]:
         assert "_h" not in lib.config_name(M, N, K), (M, N, K)
@@ -212,7 +212,7 @@ def test_mixed_plan_names_on_the_host(lib):
         assert lib.config_name(M, N, K) == big + "_k1_g4_m2", (M, N, K)
         assert lib.workspace_size(M, N, K) == 0
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 28672, 8192),
-                    (1024, 28672, 4096), (1024, 10240, 8192), (256, 8192, 8192)]:
+                    (1024, 28672, 4096), (2048, 5376, 8192), (256, 8192, 8192)]:
         assert "_m" not in lib.config_name(M, N, K), (M, N, K)
 
     def rc(name):

@@ -720,13 +720,15 @@ def test_random_mixed_plans_bit_exact():
         assert rep["ok"], (name, (M, N, K), rep)
 
 
-@pytest.mark.parametrize("M,N,K,kind", [(1024, 10240, 8192, "_h"), (2048, 10240, 8192, "_m2")])
-def test_automatic_split_plans_on_a_qkv_shape(M, N, K, kind):
-    """A 70B-class fused QKV projection (N = 10240, K = 8192) at 1024 and
-    2048 tokens: the tiles make 1.25 passes over the CUs, and the automatic
-    plan is a hybrid (256 x 128 tiles, the tail split along K) or a mixed one
-    (256 x 256 tiles, the tail on 128 x 128 tiles); full rows and columns on
-    both sides of the split column are checked against the oracle."""
+@pytest.mark.parametrize("M,N,K,kind,n1", [(2048, 5376, 8192, "_h", 4096),
+                                           (2048, 10240, 8192, "_m2", 8192)])
+def test_automatic_split_plans_on_a_qkv_shape(M, N, K, kind, n1):
+    """Shapes whose tiles make 1.31 and 1.25 passes over the CUs (the second
+    a 70B-class fused QKV projection at 2048 tokens): the automatic plan is a
+    hybrid (256 x 128 tiles, the tail from column n1 split along K) or a
+    mixed one (256 x 256 tiles, the tail on 128 x 128 tiles); full rows and
+    columns on both sides of the split column are checked against the
+    oracle."""
     import dense_gemm_bf16_amd as g
 
     plan = g.config_name(M, N, K)
@@ -737,7 +739,7 @@ def test_automatic_split_plans_on_a_qkv_shape(M, N, K, kind):
     got = run_gemm(A, B)
     o = _oracle()
     rows = np.array([0, 1, 255, 256, M // 2 + 3, M - 1])
-    cols = np.array([0, 8191, 8192, 8193, 9000, 10239])
+    cols = np.array([0, n1 - 1, n1, n1 + 1, (n1 + N) // 2, N - 1])
     r16, r64 = o.gemm(np.ascontiguousarray(A[rows]), B)
     rep = check_bf16(got[rows], r16, r64, K, 1.0, K ** -0.5)
     print("rows", rep, flush=True)

@@ -162,6 +162,17 @@ def test_choose_entries_keeps_still_best_table_rows():
     assert got == [(1, 2, 3, "p_old"), (4, 5, 6, "q_new"), (9, 9, 9, "s_new")]
 
 
+def test_choose_entries_keeps_rows_of_shapes_not_swept():
+    """A sweep over some shapes leaves the table rows of the others as they
+    are (a partial sweep must not drop them)."""
+    from dense_gemm_bf16_amd.tune import choose_entries
+
+    old = {(1, 2, 3): "p_old", (4, 5, 6): "q_old"}
+    results = {"7x8x9": {"best": "r_new", "us": 9.0, "auto": ["r_rule", 10.0]}}
+    got = choose_entries(results, old, 0.02)
+    assert got == [(7, 8, 9, "r_new"), (1, 2, 3, "p_old"), (4, 5, 6, "q_old")]
+
+
 def test_read_table_round_trip(tmp_path):
     from dense_gemm_bf16_amd.tune import read_table, write_table
 
